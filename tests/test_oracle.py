@@ -1,0 +1,473 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something the pages print, a closed form, an
+invariant, a textbook algorithm (brute force, Walsh-Hadamard) or a library
+routine, chosen so that a plausible slip (transposed Kronecker factor, column
+instead of row convention, dropped clip, log2-based exponent, ties away from
+zero, lost sign of zero, wrong nibble order) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+
+from oracle import batquant as ob
+from oracle import scalar as osc
+from tests.conftest import golden_path
+from workloads import gen
+
+# ---------------------------------------------------------------- E2M1 format
+
+
+def _read_grid():
+    with open(golden_path("e2m1_grid.txt")) as f:
+        rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+    return [float(t) for t in rows[0].split()]
+
+
+def test_e2m1_positive_values_match_pages():
+    printed = _read_grid()
+    assert printed == [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    pos = sorted(set(ob.e2m1_decode(np.arange(16))) - {0.0})
+    assert [v for v in pos if v > 0] == printed
+    assert [v for v in pos if v < 0] == [-v for v in reversed(printed)]
+
+
+def test_e2m1_decode_codes_and_signed_zero():
+    vals = ob.e2m1_decode(np.arange(16))
+    assert list(vals[:8]) == [0.0] + _read_grid()
+    assert list(vals[8:]) == [-0.0] + [-v for v in _read_grid()]
+    assert np.signbit(vals[8]) and not np.signbit(vals[0])
+
+
+def _sweep_values():
+    grid = np.arange(-8 * 4096, 8 * 4096 + 1, dtype=np.float64) / 4096.0
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    extra = []
+    for m in np.concatenate([mids, -mids]):
+        f = np.float32(m)
+        extra += [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    extra += [-0.0, 0.0, 6.0, -6.0, 7.999, -7.999]
+    return np.concatenate([grid, np.array(extra, dtype=np.float64)])
+
+
+def test_e2m1_round_equals_brute_force_nearest():
+    """Vectorised rounding (midpoint counting) equals an exhaustive nearest-value
+    search with ties to the even code, on every multiple of 2^-12 in [-8, 8] and
+    on each midpoint and its fp32 neighbours."""
+    v = _sweep_values()
+    got = ob.e2m1_round(v)
+    signed = np.array([(c, ob.e2m1_decode(c)) for c in range(16)], dtype=object)
+    for x, c in zip(v, got):
+        # brute force over all 16 codes; prefer the even magnitude code on ties
+        best = None
+        for code, val in signed:
+            if math.copysign(1.0, val) != math.copysign(1.0, x) and val != 0.0:
+                continue
+            if (code & 8) != (8 if math.copysign(1.0, x) < 0 else 0):
+                continue
+            d = abs(abs(x) - abs(val))
+            key = (d, (code & 7) % 2)
+            if best is None or key < best[0]:
+                best = (key, code)
+        assert c == best[1], (x, c, best)
+        assert osc.round_e2m1(float(x)) == c
+
+
+def test_e2m1_round_properties():
+    v = _sweep_values()
+    v = v[np.argsort(v, kind="stable")]
+    codes = ob.e2m1_round(v)
+    deq = ob.e2m1_decode(codes)
+    # monotone non-decreasing in value
+    assert np.all(np.diff(deq) >= 0)
+    # within half the local grid step for |v| <= 6; saturates beyond
+    grid = np.array(ob.E2M1_GRID)
+    for x, d in zip(v, deq):
+        ax = abs(x)
+        if ax <= 6.0:
+            hi = grid[np.searchsorted(grid, ax)] if ax < 6 else 6.0
+            lo = grid[max(np.searchsorted(grid, ax, side="right") - 1, 0)]
+            assert abs(abs(d) - ax) <= (hi - lo) / 2 + 1e-15
+        else:
+            assert abs(d) == 6.0
+    # every grid value is a fixed point
+    for c in range(16):
+        assert ob.e2m1_round(ob.e2m1_decode(c)) == c
+
+
+def test_e2m1_ties_go_to_even_code_not_away_from_zero():
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0, 2, 2, 4, 4, 6, 6]  # even codes: 0, 1.0, 1.0, 2, 2, 4, 4
+    assert list(ob.e2m1_round(np.array(mids))) == want
+    assert list(ob.e2m1_round(-np.array(mids))) == [w | 8 for w in want]
+
+
+def test_negative_values_rounding_to_zero_keep_sign():
+    assert ob.e2m1_round(np.array([-0.1]))[0] == 8
+    assert ob.e2m1_round(np.array([-0.0]))[0] == 8
+    assert ob.e2m1_round(np.array([0.1]))[0] == 0
+
+
+# ----------------------------------------------------------------- scale rule
+
+
+def test_shared_exponent_closed_form_at_powers_of_two():
+    for k in range(-120, 126):
+        p = np.float32(2.0 ** k)
+        below = np.nextafter(p, np.float32(0))
+        assert ob.shared_exponent(np.array([p]))[0] == max(k - 2, -127)
+        assert ob.shared_exponent(np.array([below]))[0] == max(k - 3, -127)
+        assert osc.scale_exponent(float(p)) == max(k - 2, -127)
+        assert osc.scale_exponent(float(below)) == max(k - 3, -127)
+    assert ob.shared_exponent(np.array([0.0]))[0] == -127
+
+
+def test_shared_exponent_puts_amax_in_4_to_8():
+    rng = np.random.default_rng(7)
+    amax = np.exp(rng.uniform(-60, 60, 20000)).astype(np.float32).astype(np.float64)
+    e = ob.shared_exponent(amax)
+    v = np.ldexp(amax, -e)
+    assert np.all((v >= 4.0) & (v < 8.0))
+
+
+def test_log2_shortcut_is_caught():
+    """The pin above catches a floor(np.log2(.)) exponent: just below a power of
+    two, the float32 log2 rounds up to the integer."""
+    below = np.nextafter(np.float32(8.0), np.float32(0))
+    naive = int(np.floor(np.log2(below))) - 2
+    assert naive != ob.shared_exponent(np.array([below]))[0]
+
+
+def _read_worked():
+    sec, amax_rows, block = None, [], {}
+    with open(golden_path("mx_worked_examples.txt")) as f:
+        for ln in f:
+            ln = ln.strip()
+            if not ln or ln.startswith("#"):
+                continue
+            if ln.startswith("["):
+                sec = ln
+                continue
+            if sec == "[amax]":
+                a, s, c = ln.split()
+                amax_rows.append((np.float32(a), int(s), int(c)))
+            else:
+                key, *vals = ln.split()
+                block[key] = vals
+    return amax_rows, block
+
+
+def test_worked_examples():
+    amax_rows, block = _read_worked()
+    for amax, sbyte, code in amax_rows:
+        y = np.zeros((1, 32), dtype=np.float32)
+        y[0, 3] = amax
+        codes, scales, _ = ob.clip_and_quantize(y, None, None)
+        assert scales[0, 0] == sbyte, amax
+        assert codes[0, 3] == code, amax
+        assert np.all(codes[0, np.arange(32) != 3] == 0)
+    y = np.zeros((1, 32), dtype=np.float32)
+    vals = np.array([float(t) for t in block["values"]], dtype=np.float32)
+    y[0, : len(vals)] = vals
+    codes, scales, _ = ob.clip_and_quantize(y, None, None)
+    assert scales[0, 0] == int(block["scale"][0])
+    assert list(codes[0, : len(vals)]) == [int(t) for t in block["codes"]]
+    # scalar form agrees
+    c2, s2 = osc.quantize_block([float(v) for v in y[0]], 1.0, 1.0)
+    assert c2 == list(codes[0]) and s2 == scales[0, 0]
+
+
+def test_zero_block():
+    codes, scales, _ = ob.clip_and_quantize(np.zeros((2, 64), np.float32), None, None)
+    assert np.all(scales == 0) and np.all(codes == 0)
+
+
+def test_pack_low_nibble_is_even_element():
+    codes = np.array([[1, 2, 3, 4, 15, 0]], dtype=np.uint8)
+    packed = ob.pack_codes(codes)
+    assert list(packed[0]) == [0x21, 0x43, 0x0F]
+    assert np.array_equal(ob.unpack_codes(packed), codes)
+
+
+def test_dequantize_uses_block_scale():
+    codes = np.zeros((1, 64), np.uint8)
+    codes[0, 0] = 7  # 6
+    codes[0, 33] = 0xA  # -1
+    deq = ob.dequantize(codes, np.array([[127 + 3, 127 - 2]], np.uint8))
+    assert deq[0, 0] == 48.0 and deq[0, 33] == -0.25 and np.count_nonzero(deq) == 2
+
+
+# --------------------------------------------------------------- clip ratios
+
+
+def test_clip_ratio_matches_library_sigmoid():
+    x = np.random.default_rng(3).normal(3, 2, 5000).astype(np.float32)
+    r = ob.clip_ratio(x)
+    assert r.dtype == np.float32
+    assert np.array_equal(r, scipy.special.expit(x.astype(np.float64)).astype(np.float32))
+    assert ob.clip_ratio(np.array([0.0]))[0] == np.float32(0.5)
+    assert ob.clip_ratio(np.array([40.0]))[0] == np.float32(1.0)
+    assert all(osc.sigmoid_f32(float(v)) == float(w) for v, w in zip(x[:200], r[:200]))
+
+
+# ----------------------------------------------------------- clip semantics
+
+
+def test_clip_bounds_are_ratio_times_block_max_and_min():
+    """Values are clamped to [r_lo*min, r_hi*max] of their own block and the scale
+    follows the clamped block."""
+    y = np.zeros((1, 32), np.float32)
+    y[0, :4] = [10.0, -4.0, 1.0, -1.0]
+    r_hi = np.array([0.5], np.float32)
+    r_lo = np.array([0.25], np.float32)
+    codes, scales, z = ob.clip_and_quantize(y, r_hi, r_lo)
+    assert z[0, 0] == 5.0 and z[0, 1] == -1.0 and z[0, 2] == 1.0 and z[0, 3] == -1.0
+    # amax 5 -> e = 0; 5 is a tie -> 4 (code 6)
+    assert scales[0, 0] == 127 and codes[0, 0] == 6
+    # without the clip the scale would follow 10
+    _, s0, _ = ob.clip_and_quantize(y, None, None)
+    assert s0[0, 0] == 128
+
+
+def test_clip_single_sign_block_order():
+    """All-positive block with r_lo*min > r_hi*max: the fixed order
+    min(max(y, l), u) maps every element to u."""
+    y = np.full((1, 32), 2.0, np.float32)
+    y[0, 0] = 2.5
+    r_hi = np.array([0.5], np.float32)  # u = 1.25
+    r_lo = np.array([0.9], np.float32)  # l = 1.8
+    _, _, z = ob.clip_and_quantize(y, r_hi, r_lo)
+    assert np.all(z == np.float32(1.25))
+    c2, s2 = osc.quantize_block([float(v) for v in y[0]], 0.5, float(np.float32(0.9)))
+    codes, scales, _ = ob.clip_and_quantize(y, r_hi, r_lo)
+    assert c2 == list(codes[0]) and s2 == scales[0, 0]
+
+
+# ---------------------------------------------------------------- transform
+
+
+@pytest.mark.parametrize("a", gen.SWEEP_A)
+def test_kron_block_matrix_equals_explicit_loops_and_factored_form(a):
+    b = 32 // a
+    rng = np.random.default_rng(a)
+    A = rng.standard_normal((a, a))
+    B = rng.standard_normal((3, b, b))
+    P = ob.block_matrices(A, B)
+    for i in range(3):
+        assert np.array_equal(P[i], np.array(osc.block_matrix(A.tolist(), B[i].tolist())))
+        assert np.array_equal(P[i], np.kron(B[i], A))
+    X = rng.standard_normal((5, 96))
+    Y = ob.transform(X, P)
+    # factored "two small matmuls" on the b x a tile: Y_b = B_i^T X_b A
+    for i in range(3):
+        Xb = X[:, 32 * i: 32 * i + 32].reshape(5, b, a)
+        Yf = np.einsum("rs,mrc,cd->msd", B[i], Xb, A).reshape(5, 32)
+        assert np.allclose(Y[:, 32 * i: 32 * i + 32], Yf, rtol=1e-12, atol=1e-12)
+    if a not in (1, 32) and a != b:
+        # a transposed convention (column vector, P_i x) is a different map
+        wrong = np.einsum("kj,mj->mk", P[0], X[:, :32])
+        assert not np.allclose(wrong, Y[:, :32])
+
+
+def test_kron_inverse_identity():
+    rng = np.random.default_rng(11)
+    A = np.eye(8) + 0.05 * rng.standard_normal((8, 8))
+    B = np.eye(4)[None] + 0.05 * rng.standard_normal((4, 4, 4))
+    PinvT = ob.inverse_transpose_blocks(A, B)
+    for i in range(4):
+        fac = np.kron(np.linalg.inv(B[i]), np.linalg.inv(A)).T
+        assert np.allclose(PinvT[i], fac, rtol=1e-12, atol=1e-12)
+        assert np.allclose(scipy.linalg.inv(np.kron(B[i], A)).T, PinvT[i], rtol=1e-12, atol=1e-13)
+
+
+def test_linear_layer_equivalence_without_quantisation():
+    """(X P)(P^-1 W^T) = X W^T, block by block (each 32-channel partial product
+    is preserved), with random invertible non-orthogonal factors."""
+    wl = gen.make_custom(16, 128, 24, a=4, seed=5)
+    X = ob.bf16_values(wl.X_bits)
+    W = ob.bf16_values(wl.W_bits)
+    P = ob.block_matrices(wl.A, wl.B)
+    PinvT = ob.inverse_transpose_blocks(wl.A, wl.B)
+    Xp = ob.transform(X, P)
+    Wp = ob.transform(W, PinvT)
+    ref = X @ W.T
+    assert np.allclose(Xp @ Wp.T, ref, rtol=1e-10, atol=1e-10 * np.abs(ref).max())
+    for i in range(4):
+        s = slice(32 * i, 32 * i + 32)
+        assert np.allclose(Xp[:, s] @ Wp[:, s].T, X[:, s] @ W[:, s].T, rtol=1e-10, atol=1e-12)
+
+
+def test_locality_no_output_depends_on_another_block():
+    wl = gen.make_custom(8, 256, 8, a=8, seed=9)
+    d0 = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    X2 = wl.X_bits.copy()
+    X2[:, 96:128] = gen.f64_to_bf16_bits(np.random.default_rng(1).standard_normal((8, 32)) * 30)
+    d1 = ob.act_transform_quant(X2, wl.A, wl.B, wl.alpha, wl.beta)
+    other = np.ones(256, bool)
+    other[96:128] = False
+    assert np.array_equal(d0.codes[:, other], d1.codes[:, other])
+    assert np.array_equal(np.delete(d0.scales, 3, axis=1), np.delete(d1.scales, 3, axis=1))
+    assert np.array_equal(d0.y64[:, other], d1.y64[:, other])
+    assert not np.array_equal(d0.codes[:, ~other], d1.codes[:, ~other])
+
+
+def _fwht(x):
+    """Iterative fast Walsh-Hadamard transform (natural/Sylvester order)."""
+    x = np.array(x, dtype=np.float64)
+    h = 1
+    n = x.shape[-1]
+    while h < n:
+        y = x.reshape(x.shape[:-1] + (n // (2 * h), 2, h))
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a + b, a - b
+        x = y.reshape(x.shape)
+        h *= 2
+    return x
+
+
+def test_block_hadamard_special_case_is_orthogonal_fwht():
+    """A = H8/sqrt(8), B_i = H4/2 gives P_i = H32/sqrt(32) (Sylvester), the
+    block rotation of the BRQ article (10100.com, section 5): energy preserving,
+    equal to a fast Walsh-Hadamard transform of each block."""
+    H8 = scipy.linalg.hadamard(8) / math.sqrt(8)
+    H4 = scipy.linalg.hadamard(4) / 2.0
+    P = ob.block_matrices(H8, np.stack([H4, H4]))
+    assert np.allclose(P[0], scipy.linalg.hadamard(32) / math.sqrt(32), atol=1e-15)
+    X = np.random.default_rng(2).standard_normal((6, 64))
+    Y = ob.transform(X, P)
+    assert np.allclose(np.linalg.norm(Y, axis=1), np.linalg.norm(X, axis=1), rtol=1e-13)
+    assert np.allclose(np.linalg.norm(Y[:, :32], axis=1), np.linalg.norm(X[:, :32], axis=1), rtol=1e-13)
+    ref = np.concatenate([_fwht(X[:, :32]), _fwht(X[:, 32:])], axis=1) / math.sqrt(32)
+    assert np.allclose(Y, ref, atol=1e-13)
+
+
+def test_extreme_shared_sizes():
+    rng = np.random.default_rng(4)
+    B1 = rng.standard_normal((2, 32, 32))
+    P = ob.block_matrices(np.ones((1, 1)), B1)
+    assert np.array_equal(P, B1)  # a = 1: one full private matrix per block
+    A32 = rng.standard_normal((32, 32))
+    Bs = rng.standard_normal((2, 1, 1))
+    P = ob.block_matrices(A32, Bs)
+    assert np.allclose(P[1], Bs[1, 0, 0] * A32)  # a = 32: scalar times shared
+
+
+# ------------------------------------------------------------ param counts
+
+
+def test_parameter_counts_match_pages():
+    with open(golden_path("param_counts.txt")) as f:
+        kv = dict(ln.split() for ln in f if ln.strip() and not ln.startswith("#"))
+    K = int(kv["hidden"])
+    assert ob.param_count_full_blocks(K) == int(kv["full_blocks"])
+    assert ob.param_count_naive_kron(K, 8) == int(kv["naive_kronecker"])
+    assert ob.param_count_gpk(K, 8) == int(kv["gpk"])
+    assert ob.param_count_flatquant(K) == int(kv["flatquant"])
+    lo = 100 * (1 - ob.param_count_gpk(K, 8) / ob.param_count_flatquant(K))
+    hi = 100 * (1 - ob.param_count_gpk(K, 8) / ob.param_count_naive_kron(K, 8))
+    assert math.floor(lo) == int(kv["reduction_low_percent"])
+    assert math.floor(hi) == int(kv["reduction_high_percent"])
+    # the shared-size sweep of the pages: private size is 32/|A|
+    for a in gen.SWEEP_A:
+        assert ob.param_count_gpk(K, a) == a * a + 128 * (32 // a) ** 2
+
+
+# --------------------------------------------------- scalar vs vectorised
+
+
+def test_scalar_and_vectorised_oracle_agree_on_tiny():
+    wl = gen.make_workload(1)
+    d = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    c, s = osc.act_transform_quant(wl.X_bits.tolist(), wl.A.tolist(), wl.B.tolist(),
+                                   wl.alpha.tolist(), wl.beta.tolist())
+    assert np.array_equal(d.codes, np.array(c, np.uint8))
+    assert np.array_equal(d.scales, np.array(s, np.uint8))
+
+
+def test_scalar_and_vectorised_weight_prep_agree():
+    wl = gen.make_workload(1)
+    rows = slice(0, 48)
+    d = ob.weight_prep(wl.W_bits[rows], wl.A, wl.B, wl.walpha[rows], wl.wbeta[rows])
+    c, s = osc.weight_prep(wl.W_bits[rows].tolist(), wl.A.tolist(), wl.B.tolist(),
+                           wl.walpha[rows].tolist(), wl.wbeta[rows].tolist())
+    assert np.array_equal(d.codes, np.array(c, np.uint8))
+    assert np.array_equal(d.scales, np.array(s, np.uint8))
+    dn = ob.weight_prep(wl.W_bits[rows], wl.A, wl.B, None, None)
+    c, s = osc.weight_prep(wl.W_bits[rows].tolist(), wl.A.tolist(), wl.B.tolist())
+    assert np.array_equal(dn.codes, np.array(c, np.uint8))
+
+
+# -------------------------------------------------------------------- GEMM
+
+
+def test_gemm_fp64_equals_exact_rationals_on_tiny():
+    wl = gen.make_workload(1)
+    x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    w = ob.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha, wl.wbeta)
+    Y = ob.gemm(x.codes, x.scales, w.codes, w.scales)
+    rows, cols = slice(0, 12), slice(0, 10)
+    exact = osc.gemm_exact(x.codes[rows].tolist(), x.scales[rows].tolist(),
+                           w.codes[cols].tolist(), w.scales[cols].tolist())
+    assert np.array_equal(Y[rows, cols], np.array([[float(v) for v in r] for r in exact]))
+
+
+def test_end_to_end_approximates_unquantised_layer():
+    """Q(XP) Q(P^-1 W^T) stays close to X W^T (a loose sanity bound: 4-bit
+    operands), and both quantised sides are needed to match the oracle chain."""
+    wl = gen.make_workload(1)
+    x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    w = ob.weight_prep(wl.W_bits, wl.A, wl.B, None, None)
+    Y = ob.gemm(x.codes, x.scales, w.codes, w.scales)
+    ref = ob.unquantized_layer(wl.X_bits, wl.W_bits)
+    rel = np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    assert rel < 0.35
+
+
+# --------------------------------------------------------- decision intervals
+
+
+def test_identity_factors_are_exact_and_free_of_exemptions():
+    wl = gen.make_workload(1)
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (8, 1, 1))
+    logit = np.full(8, 40.0, np.float32)  # ratio 1.0: the plain OCP MX quantiser
+    d = ob.act_transform_quant(wl.X_bits, A, B, logit, logit, exact=True)
+    X = ob.bf16_values(wl.X_bits).astype(np.float32)
+    codes, scales, _ = ob.clip_and_quantize(X, None, None)
+    assert np.array_equal(d.codes, codes) and np.array_equal(d.scales, scales)
+    assert d.n_exempt == 0
+
+
+def test_fp32_evaluation_only_flips_exempt_decisions():
+    """Evaluate the transform the way a GPU kernel may (fp32, factored, any
+    order): every decision the interval analysis calls fixed must be identical."""
+    for cfg in (1, 4):
+        wl = gen.make_workload(cfg, with_weights=False)
+        d = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+        X = ob.bf16_values(wl.X_bits).astype(np.float32)
+        rows, K = X.shape
+        nb = K // 32
+        Xb = X.reshape(rows, nb, 4, 8)
+        T = np.einsum("mirc,cd->mird", Xb, wl.A.astype(np.float32), dtype=np.float32)
+        Y32 = np.einsum("irs,mird->misd", wl.B.astype(np.float32), T, dtype=np.float32).reshape(rows, K)
+        codes, scales, _ = ob.clip_and_quantize(Y32, ob.clip_ratio(wl.alpha), ob.clip_ratio(wl.beta))
+        fixed_blk = ~d.block_free
+        assert np.array_equal(scales[fixed_blk], d.scales[fixed_blk])
+        fixed = ~(d.elem_free | np.repeat(d.block_free, 32, axis=1) | d.zero_sign_free)
+        assert np.array_equal(codes[fixed], d.codes[fixed])
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_exempt_window_stays_narrow(cfg):
+    """The free set is the rigorous fp32 window (about 2e-6 of a block's absolute
+    sum); on these workloads it covers a few 1e-5 of the elements at most.  A
+    bound blown up by a slip (wrong gamma, S not in absolute values) fails here."""
+    M = {1: None, 2: 256, 3: 128, 4: None}[cfg]
+    wl = gen.make_workload(cfg, M=M, with_weights=False)
+    d = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    n = d.codes.size
+    assert d.n_exempt / n < 5e-5, (d.n_exempt, n)
+    assert not np.any(d.zero_sign_free)
