@@ -1,0 +1,237 @@
+"""Benchmark of the BATQuant W4A4 hot path on one MI355X.
+
+One step = the whole online path for one batch: the fused activation block
+transform + clip + MXFP4 quantisation kernel followed by the W4A4 MXFP4 GEMM
+(bf16 output).  The weight side (P^-1 W^T, clip, quantise) is offline and runs
+once before timing.  Default workload: the up/gate projection prefill layer,
+X 2048 x 4096 bf16 and W 12288 x 4096 bf16, shared factor 8x8 / private 4x4.
+
+Inputs are resident in HBM when timing starts.  Steps rotate through several
+copies of every buffer (more bytes than the 256 MB Infinity Cache) so a step
+cannot be served from the cache a previous step filled.
+
+Prints ONE JSON line.  ``value`` is the step throughput in TFLOP/s of W4A4 GEMM
+work (2 M N K per step) including the activation kernel's time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix, published
+METRIC = "transform+MXFP4-quant GB/s (% HBM peak); MXFP4 GEMM TFLOPS (% MFMA peak)"
+CACHE_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--a", type=int, default=8, help="shared factor size (config 5 sweep)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="token rows in the oracle sample")
+    ap.add_argument("--cpu-cols", type=int, default=2048, help="weight rows in the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_digest(name: str) -> str:
+    path = os.path.join(ROOT, "w4a4_bit_gemm_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_digest(kernel_file)
+    with open(path) as f:
+        for ln in f:
+            parts = ln.split()
+            if len(parts) >= 4 and not ln.startswith("#") and parts[0] == kernel_file and parts[1] == want:
+                return float(parts[2]) + float(parts[3])  # fetched + written bytes, calibrated
+    return None
+
+
+def cpu_baseline(wl, rows_n: int, cols_n: int):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import threadpoolctl
+
+    from oracle import batquant as ob
+
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(wl.M, size=min(rows_n, wl.M), replace=False))
+    cols = np.sort(rng.choice(wl.N, size=min(cols_n, wl.N), replace=False))
+    wprep = ob.weight_prep(wl.W_bits[cols], wl.A, wl.B, wl.walpha[cols], wl.wbeta[cols])  # offline, untimed
+    t0 = time.perf_counter()
+    x = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
+    t1 = time.perf_counter()
+    ob.gemm(x.codes, x.scales, wprep.codes, wprep.scales)
+    t2 = time.perf_counter()
+    t_act = (t1 - t0) * wl.M / len(rows)
+    t_gemm = (t2 - t1) * (wl.M / len(rows)) * (wl.N / len(cols))
+    flops = 2.0 * wl.M * wl.N * wl.K
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([d.get("num_threads", 1) for d in info] or [1])
+    return {
+        "value": flops / (t_act + t_gemm) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} of {wl.M} token rows through the oracle activation path "
+                   f"({t1 - t0:.2f} s) and their GEMM against {len(cols)} of {wl.N} prepared weight rows "
+                   f"({t2 - t1:.2f} s); step time extrapolated linearly to the full layer; "
+                   f"host cores visible: {len(os.sched_getaffinity(0))}"),
+        "seconds_measured": t2 - t0,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import w4a4_bit_gemm_amd as w
+    from workloads import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = gen.make_workload(args.config, a=args.a)
+    M, K, N = wl.M, wl.K, wl.N
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    X0 = bf16(wl.X_bits)
+    A = f32(wl.A)
+    B = f32(wl.B)
+    rh = f32(w.clip_ratios(wl.alpha))
+    rl = f32(w.clip_ratios(wl.beta))
+    Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)  # offline
+    torch.cuda.synchronize()
+
+    set_bytes = M * K * 2 + M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
+    nsets = max(2, int(np.ceil(2.2 * CACHE_BYTES / set_bytes)))
+    nsets = min(nsets, 16)
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(
+            X=X0.clone(), Wq=Wq0.clone(), Ws=Ws0.clone(),
+            Xq=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            Xs=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+            Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if ev is not None:
+            ev[0].record()
+        w.act_transform_quant(s["X"], A, B, rh, rl, out=(s["Xq"], s["Xs"]))
+        if ev is not None:
+            ev[1].record()
+        w.mxfp4_gemm(s["Xq"], s["Xs"], s["Wq"], s["Ws"], out=s["Y"])
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel durations with HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_act = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+
+    flops = 2.0 * M * N * K
+    act_bytes = M * K * 2 + M * K // 2 + M * K // 32  # algorithmic: read bf16, write codes + scales
+    gemm_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
+    act_gbs = act_bytes / t_act.mean() / 1e9
+    gemm_tflops = flops / t_gemm.mean() / 1e12
+    ai = flops / gemm_bytes
+    gemm_hbm_bound = ai < MXFP4_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gemm_hbm_bound:
+        gemm_roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm.mean() / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s"}
+    else:
+        gemm_roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    gemm_roof["frac"] = gemm_roof["achieved"] / gemm_roof["peak"]
+    act_roof = {"bound": "hbm", "achieved": act_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": act_gbs / HBM_PEAK_GBS}
+    dominant_is_gemm = t_gemm.mean() >= t_act.mean()
+    roof = dict(gemm_roof if dominant_is_gemm else act_roof)
+    traffic = load_traffic("mxfp4_gemm.hip" if dominant_is_gemm else "transform_quant.hip")
+    roof["traffic"] = traffic
+    roof["kernel"] = "mxfp4_gemm_kernel" if dominant_is_gemm else "transform_quant_kernel"
+    act_roof["traffic"] = load_traffic("transform_quant.hip")
+
+    out = {
+        "metric": METRIC,
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), "
+                        f"W {N}x{K} bf16 N(0,0.02) pre-packed offline; GPK a={wl.a} b={wl.b}; "
+                        f"step = act transform+clip+MXFP4 quant + MXFP4 GEMM (bf16 out)",
+            "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets,
+        },
+        "roofline": roof,
+        "kernels": {
+            "transform_quant": {"us": float(t_act.mean() * 1e6), "GB/s": act_gbs,
+                                "frac_hbm": act_gbs / HBM_PEAK_GBS, "algorithmic_bytes": act_bytes,
+                                "roofline": act_roof},
+            "mxfp4_gemm": {"us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
+                           "frac_mfma": gemm_tflops / MXFP4_PEAK_TFLOPS, "flops": flops,
+                           "operand_output_bytes": gemm_bytes},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows, args.cpu_cols)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * batq.h — C ABI of the BATQuant W4A4 deployment path on MI355X (gfx950).
+ *
+ * What the library computes (BATQuant pages; cited by page and section):
+ *   A linear layer Y = X W^T is rewritten as Y = (X P)(P^-1 W^T).  P is block
+ *   diagonal over the 32-channel MXFP4 blocks, each block P_i = B_i (x) A with one
+ *   shared a x a factor A and a private b x b factor B_i, a * b = 32
+ *   [en.papernotes.org BATQuant note, Key Designs §1-§2; nubint.ai review, 提案手法].
+ *   The activation side is transformed online, clipped block-wise with
+ *   sigmoid-mapped ratios on the block max/min, and quantised to MXFP4; the
+ *   weight side P^-1 W^T is fused and quantised offline; the two quantised
+ *   operands meet in a W4A4 GEMM [en.papernotes.org, Overall Architecture;
+ *   Key Designs §3; A Worked Example].
+ *
+ * Conventions shared by every entry point:
+ *   - Row-major everywhere.  Block i of row m is channels [32 i, 32 i + 32).
+ *   - Vec convention of the block transform (the pages leave it open): row
+ *     vector, y_b = x_b P_i with P_i[a r + c][a r' + c'] = B_i[r][r'] A[c][c'].
+ *   - MXFP4 storage: codes [rows][K/2] bytes, element 2j in the low nibble of
+ *     byte j; code = sign << 3 | magnitude index into {0,.5,1,1.5,2,3,4,6};
+ *     scales [rows][K/32] bytes, UE8M0 (value 2^(byte-127)).
+ *   - Scale exponent floor(log2 amax) - 2 clamped to [-127, 127] (OCP MX v1.0
+ *     rule), elements rounded to nearest E2M1 with ties to the even code, |v| >= 6
+ *     saturating to 6, sign kept (a negative value rounding to 0 is code 0x8).
+ *   - Device pointers unless the name ends in _host.  Every device call is
+ *     asynchronous on `stream` (0 = the null stream).  The library never
+ *     allocates, frees or synchronises, keeps no pointer after returning and
+ *     holds no mutable global state: calls on distinct streams are thread-safe.
+ *   - The caller owns every buffer and keeps it alive until the stream work
+ *     completes.
+ *   - Errors: every argument check runs on the host before any HIP call and
+ *     returns a status without launching anything; a launch failure reported by
+ *     hipGetLastError maps to BATQ_ERR_HIP.  Nothing is printed, nothing thrown.
+ *   - Non-finite inputs are outside the defined domain (results unspecified,
+ *     no fault).
+ */
+#ifndef BATQ_H
+#define BATQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BATQ_ABI_VERSION 1
+
+typedef enum {
+  BATQ_OK = 0,
+  BATQ_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  BATQ_ERR_SHAPE = 2,       /* negative size, K not a positive multiple of 32,
+                               leading dimension smaller than K, a*b != 32        */
+  BATQ_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks the stated
+                               alignment                                          */
+  BATQ_ERR_UNSUPPORTED = 4, /* a outside {1,2,4,8,16,32} or unknown output type   */
+  BATQ_ERR_SINGULAR = 5,    /* a factor is singular or too ill-conditioned        */
+  BATQ_ERR_HIP = 6          /* the HIP runtime rejected a launch                  */
+} batq_status;
+
+typedef enum { BATQ_OUT_BF16 = 0, BATQ_OUT_F32 = 1 } batq_out_dtype;
+
+/* BATQ_ABI_VERSION of the built library. */
+int batq_abi_version(void);
+
+/* Static English text of a status code ("unknown status" for other values). */
+const char* batq_status_str(int status);
+
+/* ---------------------------------------------------------------- host helpers
+ * Host-only; no HIP call.
+ */
+
+/* Clip ratios r = sigmoid(logit), evaluated in double and rounded once to float:
+ * the deployed form of the learnable block-wise clipping parameters, which a
+ * sigmoid maps into (0, 1) [en.papernotes.org, Key Designs §3].
+ * logits_host, ratios_host: n floats each (may alias).  n >= 0.
+ * Errors: NULL (either pointer NULL with n > 0), SHAPE (n < 0). */
+batq_status batq_clip_ratios(const float* logits_host, float* ratios_host, int64_t n);
+
+/* Inverse-transposed GPK factors for the offline weight side.  Because
+ * (B_i (x) A)^-T = B_i^-T (x) A^-T, the weight transform W P^-T is the same
+ * block transform with factors A^-T and B_i^-T [en.papernotes.org, Key Designs
+ * §1-§2: the inverse is absorbed into the weights].
+ * A_host: [a][a] floats; B_host: [nblocks][b][b] floats.
+ * AinvT_host: [a][a]; BinvT_host: [nblocks][b][b] (outputs, float, computed by
+ * Gauss-Jordan elimination with partial pivoting in double, rounded once).
+ * Errors: NULL; SHAPE (nblocks < 0, a*b != 32); UNSUPPORTED (a not a power of two
+ * in 1..32); SINGULAR (a zero pivot or an estimated 1-norm condition number above
+ * 1e6 for any factor; outputs then unspecified). */
+batq_status batq_gpk_invert(int32_t a, int32_t b, int64_t nblocks, const float* A_host,
+                            const float* B_host, float* AinvT_host, float* BinvT_host);
+
+/* --------------------------------------------------------------- device calls */
+
+/* Online activation path, one fused kernel: per row m and block i,
+ *   y = x_b (B_i (x) A)                      (block transform, fp32 accumulation)
+ *   z = min(max(y, r_lo[i] * min(y)), r_hi[i] * max(y))   (block-wise clipping)
+ *   Xs[m][i] = e + 127, Xq codes = RNE_E2M1(z / 2^e)      (MXFP4 quantisation)
+ * [en.papernotes.org, A Worked Example: transform block by block, clip, quantise;
+ *  Key Designs §1-§3].
+ * X_bf16: [M][ldx] bfloat16, row stride ldx elements (ldx >= K, ldx % 8 == 0,
+ *         X 16-byte aligned).
+ * A: [a][a] float; B: [K/32][b][b] float (the factors, row-major).
+ * r_hi, r_lo: [K/32] float clip ratios (batq_clip_ratios), or both NULL for no
+ *         clipping.  One NULL and one non-NULL is BATQ_ERR_NULL.
+ * Xq: [M][K/2] bytes (16-byte aligned); Xs: [M][K/32] bytes.
+ * M == 0 is a no-op.  Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, HIP. */
+batq_status batq_act_transform_quant(const void* X_bf16, int64_t M, int64_t K, int64_t ldx,
+                                     int32_t a, int32_t b, const float* A, const float* B,
+                                     const float* r_hi, const float* r_lo,
+                                     uint8_t* Xq, uint8_t* Xs, hipStream_t stream);
+
+/* Offline weight side: W' = W P^-T block by block (the transpose of P^-1 W^T),
+ * clipped with one ratio pair per (output row, block), MXFP4-quantised with the
+ * same rules [en.papernotes.org, Overall Architecture; Key Designs §3: weights
+ * receive analogous treatment].  Run once per layer; round-to-nearest, no GPTQ.
+ * W_bf16: [N][ldw] bfloat16 (ldw >= K, ldw % 8 == 0, 16-byte aligned).
+ * AinvT: [a][a]; BinvT: [K/32][b][b] float — the outputs of batq_gpk_invert.
+ * wr_hi, wr_lo: [N][K/32] float ratios, or both NULL for no clipping.
+ * Wq: [N][K/2] (16-byte aligned); Ws: [N][K/32].
+ * N == 0 is a no-op.  Errors: as batq_act_transform_quant. */
+batq_status batq_weight_prep(const void* W_bf16, int64_t N, int64_t K, int64_t ldw,
+                             int32_t a, int32_t b, const float* AinvT, const float* BinvT,
+                             const float* wr_hi, const float* wr_lo,
+                             uint8_t* Wq, uint8_t* Ws, hipStream_t stream);
+
+/* W4A4 GEMM on MXFP4 operands: Y[m][n] = sum_k deq(Xq)[m][k] * deq(Wq)[n][k] with
+ * FP32 accumulation on the block-scaled MFMA units, written as float or as
+ * bfloat16 (round to nearest even) [en.papernotes.org, Key Designs §1 and §4:
+ * the product Q(XP) Q(P^-1 W^T); all linear layers use low-bit matmul].
+ * Xq: [M][K/2], Xs: [M][K/32], Wq: [N][K/2], Ws: [N][K/32] (code rows 16-byte
+ * aligned, which K % 32 == 0 gives for 16-byte aligned bases).
+ * Y: [M][N] of the chosen type, 4-byte aligned.
+ * M == 0 or N == 0 is a no-op.  Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, HIP. */
+batq_status batq_mxfp4_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                            const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
+                            batq_out_dtype out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BATQ_H */

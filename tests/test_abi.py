@@ -1,0 +1,130 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, validates arguments before any HIP call, and its host helpers
+agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import batquant as ob
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "batq.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, SINGULAR, HIP = range(7)
+FAKE = 0x10000  # aligned address never dereferenced: every case below fails a check first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from w4a4_bit_gemm_amd import binding
+
+    return binding._load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(batq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("batq_act_transform_quant", "batq_weight_prep", "batq_mxfp4_gemm", "batq_gpk_invert",
+              "batq_clip_ratios", "batq_abi_version", "batq_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.batq_abi_version() == 1
+    for s in range(7):
+        assert lib.batq_status_str(s) and lib.batq_status_str(s) != b"unknown status"
+    assert lib.batq_status_str(99) == b"unknown status"
+
+
+def _tq(lib, fn, x=FAKE, M=4, K=64, ld=64, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0, q=FAKE, s=FAKE):
+    return getattr(lib, fn)(x, M, K, ld, a, b, A, B, rh, rl, q, s, None)
+
+
+@pytest.mark.parametrize("fn", ["batq_act_transform_quant", "batq_weight_prep"])
+def test_transform_argument_checks(lib, fn):
+    assert _tq(lib, fn, x=0) == NULL
+    assert _tq(lib, fn, A=0) == NULL
+    assert _tq(lib, fn, B=0) == NULL
+    assert _tq(lib, fn, q=0) == NULL
+    assert _tq(lib, fn, s=0) == NULL
+    assert _tq(lib, fn, rh=FAKE, rl=0) == NULL
+    assert _tq(lib, fn, K=48, ld=64) == SHAPE
+    assert _tq(lib, fn, K=0, ld=0) == SHAPE
+    assert _tq(lib, fn, M=-1) == SHAPE
+    assert _tq(lib, fn, ld=32) == SHAPE
+    assert _tq(lib, fn, a=8, b=8) == SHAPE
+    assert _tq(lib, fn, a=-1, b=-32) == UNSUP
+    assert _tq(lib, fn, x=FAKE + 2) == ALIGN
+    assert _tq(lib, fn, q=FAKE + 8) == ALIGN
+    assert _tq(lib, fn, ld=68) == ALIGN
+    # empty input: a no-op that returns before touching the GPU
+    assert _tq(lib, fn, M=0) == OK
+
+
+def test_gemm_argument_checks(lib):
+    f = lib.batq_mxfp4_gemm
+    assert f(0, FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, 0, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 48, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, -4, 4, 64, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 7, None) == UNSUP
+    assert f(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, FAKE + 2, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, FAKE, 0, None) == OK
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, FAKE, 1, None) == OK
+
+
+def test_clip_ratios_match_oracle():
+    from w4a4_bit_gemm_amd import binding
+
+    x = np.random.default_rng(0).normal(3, 3, 4096).astype(np.float32)
+    assert np.array_equal(binding.clip_ratios(x), ob.clip_ratio(x))
+
+
+def test_clip_ratios_errors(lib):
+    assert lib.batq_clip_ratios(None, None, 0) == OK
+    assert lib.batq_clip_ratios(None, FAKE, 3) == NULL
+    assert lib.batq_clip_ratios(FAKE, FAKE, -1) == SHAPE
+
+
+@pytest.mark.parametrize("a", [1, 2, 4, 8, 16, 32])
+def test_gpk_invert_matches_oracle_inverse(a):
+    from w4a4_bit_gemm_amd import binding
+    from workloads import gen
+
+    A, B = gen.make_factors(5, 256, a, sweep=True)
+    AinvT, BinvT = binding.gpk_invert(A, B)
+    PinvT = ob.inverse_transpose_blocks(A, B)
+    for i in range(B.shape[0]):
+        got = np.kron(BinvT[i].astype(np.float64), AinvT.astype(np.float64))
+        # each factor is the double inverse rounded once to float
+        assert np.allclose(got, PinvT[i], rtol=4e-7, atol=4e-7 * np.abs(PinvT[i]).max())
+
+
+def test_gpk_invert_rejects_singular(lib):
+    A = np.eye(8, dtype=np.float32)
+    A[3] = A[2]
+    B = np.tile(np.eye(4, dtype=np.float32), (2, 1, 1))
+    out_a = np.empty_like(A)
+    out_b = np.empty_like(B)
+    st = lib.batq_gpk_invert(8, 4, 2, A.ctypes.data, B.ctypes.data, out_a.ctypes.data, out_b.ctypes.data)
+    assert st == SINGULAR
+    B[1] = np.diag([1.0, 1e-9, 1.0, 1.0]).astype(np.float32)  # ill-conditioned private factor
+    A = np.eye(8, dtype=np.float32)
+    st = lib.batq_gpk_invert(8, 4, 2, A.ctypes.data, B.ctypes.data, out_a.ctypes.data, out_b.ctypes.data)
+    assert st == SINGULAR
+    assert lib.batq_gpk_invert(8, 8, 2, A.ctypes.data, B.ctypes.data, out_a.ctypes.data,
+                               out_b.ctypes.data) == SHAPE

@@ -1,0 +1,312 @@
+"""GPU parity: the HIP kernels through the C ABI against the CPU oracle, on the
+same seeded inputs.  Needs an MI355X; run with ``-m gpu``."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import batquant as ob
+from tests import parity
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def w():
+    import w4a4_bit_gemm_amd as w
+
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return w
+
+
+DEV = "cuda"
+
+
+def dev_bf16(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dev_f32(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def run_act(w, wl, A=None, B=None, alpha=None, beta=None, clip=True):
+    A = wl.A if A is None else A
+    B = wl.B if B is None else B
+    alpha = wl.alpha if alpha is None else alpha
+    beta = wl.beta if beta is None else beta
+    X = dev_bf16(wl.X_bits)
+    rh = dev_f32(w.clip_ratios(alpha)) if clip else None
+    rl = dev_f32(w.clip_ratios(beta)) if clip else None
+    Xq, Xs = w.act_transform_quant(X, dev_f32(A), dev_f32(B), rh, rl)
+    torch.cuda.synchronize()
+    return Xq.cpu().numpy(), Xs.cpu().numpy()
+
+
+def run_weight(w, wl, clip=True):
+    Wd = dev_bf16(wl.W_bits)
+    if clip:
+        Wq, Ws = w.prepare_weight(Wd, wl.A, wl.B, wl.walpha, wl.wbeta)
+    else:
+        Wq, Ws = w.prepare_weight(Wd, wl.A, wl.B)
+    torch.cuda.synchronize()
+    return Wq.cpu().numpy(), Ws.cpu().numpy()
+
+
+# ------------------------------------------------------------ activation path
+
+
+def test_act_tiny_matches_oracle(w):
+    note("case: act tiny (config 1, 64x256, a=8)")
+    wl = gen.make_workload(1)
+    q, s = run_act(w, wl)
+    dec = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    st = parity.compare_quant(q, s, dec, label="tiny")
+    assert st["mismatches"] == 0, st
+
+
+@pytest.mark.parametrize("M,K,a,seed", [(1, 32, 8, 1), (33, 96, 4, 2), (100, 224, 2, 3), (257, 512, 16, 4),
+                                        (31, 64, 1, 5), (77, 128, 32, 6), (300, 4096, 8, 7)])
+def test_act_ragged_shapes_and_factor_sizes(w, M, K, a, seed):
+    note(f"case: act ragged M={M} K={K} a={a}")
+    wl = gen.make_custom(M, K, 8, a=a, seed=seed)
+    q, s = run_act(w, wl)
+    dec = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    parity.compare_quant(q, s, dec, label=f"ragged {M}x{K} a={a}")
+
+
+def test_act_no_clip(w):
+    note("case: act without clipping")
+    wl = gen.make_custom(70, 256, 8, seed=11)
+    q, s = run_act(w, wl, clip=False)
+    P = ob.block_matrices(wl.A, wl.B)
+    X = ob.bf16_values(wl.X_bits)
+    dec = ob.decisions(ob.transform(X, P), ob.transform_abs_sum(X, P), None, None)
+    parity.compare_quant(q, s, dec, label="no clip")
+
+
+def test_act_identity_factors_exact_with_ties(w):
+    """A = I, B_i = I, dyadic ratios: every fp32 step is exact, so the whole
+    output must match bit for bit, including values exactly on midpoints."""
+    note("case: act identity factors, dyadic ratios, exact ties")
+    rng = np.random.default_rng(21)
+    M, K = 96, 512
+    # values on a coarse dyadic grid put many elements exactly on E2M1 midpoints
+    x = rng.integers(-48, 49, size=(M, K)) / 8.0
+    x[:, 5] *= 64
+    wl = gen.make_custom(M, K, 8, seed=21)
+    wl.X_bits = gen.f64_to_bf16_bits(x)
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (K // 32, 1, 1))
+    # logits whose float32 sigmoid is exactly 1, 0.75 or 0.5
+    lg = np.array([40.0, np.log(3.0), 0.0], dtype=np.float32)
+    alpha = lg[np.arange(K // 32) % 3]
+    beta = lg[(np.arange(K // 32) + 1) % 3]
+    assert set(ob.clip_ratio(lg).tolist()) == {1.0, 0.75, 0.5}
+    q, s = run_act(w, wl, A=A, B=B, alpha=alpha, beta=beta)
+    dec = ob.act_transform_quant(wl.X_bits, A, B, alpha, beta, exact=True)
+    codes = ob.unpack_codes(q)
+    assert np.array_equal(s, dec.scales)
+    same = (codes == dec.codes) | (dec.zero_sign_free & ((codes & 7) == 0) & ((dec.codes & 7) == 0))
+    assert same.all(), np.argwhere(~same)[:5].tolist()
+    v = np.abs(np.ldexp(dec.z32.astype(np.float64), -(dec.scales.astype(np.int64) - 127).repeat(32, axis=1)))
+    assert np.isin(v, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]).sum() > 100  # ties really exercised
+
+
+def test_act_zero_and_single_sign_blocks(w):
+    note("case: act zero blocks and single-sign blocks")
+    wl = gen.make_custom(40, 256, 8, seed=31)
+    x = ob.bf16_values(wl.X_bits)
+    x[:, 0:32] = 0.0                    # all-zero block
+    x[:, 32:64] = np.abs(x[:, 32:64]) + 1.0  # all-positive block
+    x[:, 64:96] = -np.abs(x[:, 64:96]) - 1.0  # all-negative block
+    wl.X_bits = gen.f64_to_bf16_bits(x)
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (8, 1, 1))
+    alpha = np.full(8, -1.0, np.float32)  # r_hi ~ 0.27
+    beta = np.full(8, 2.0, np.float32)    # r_lo ~ 0.88 > r_hi: l > u on positive blocks
+    q, s = run_act(w, wl, A=A, B=B, alpha=alpha, beta=beta)
+    dec = ob.act_transform_quant(wl.X_bits, A, B, alpha, beta, exact=True)
+    codes = ob.unpack_codes(q)
+    assert np.all(s[:, 0] == 0)
+    assert np.all((codes[:, :32] & 7) == 0)
+    assert np.array_equal(s, dec.scales)
+    same = (codes == dec.codes) | (dec.zero_sign_free & ((codes & 7) == 0))
+    assert same.all()
+
+
+def test_act_locality_and_determinism(w):
+    note("case: act locality (re-randomised block) and determinism")
+    wl = gen.make_custom(128, 1024, 8, seed=41)
+    q0, s0 = run_act(w, wl)
+    q1, s1 = run_act(w, wl)
+    assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
+    x2 = wl.X_bits.copy()
+    x2[:, 320:352] = gen.f64_to_bf16_bits(np.random.default_rng(5).standard_t(3, (128, 32)) * 20)
+    wl2 = gen.make_custom(128, 1024, 8, seed=41)
+    wl2.X_bits = x2
+    q2, s2 = run_act(w, wl2)
+    keep_q = np.ones(512, bool)
+    keep_q[160:176] = False
+    keep_s = np.ones(32, bool)
+    keep_s[10] = False
+    assert np.array_equal(q0[:, keep_q], q2[:, keep_q])
+    assert np.array_equal(s0[:, keep_s], s2[:, keep_s])
+    assert not np.array_equal(q0[:, ~keep_q], q2[:, ~keep_q])
+
+
+def _sample_rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    rows.update([0, M - 1])
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_act_full_config(w, cfg):
+    """Full-size activation run (the shape the benchmark times); every code of a
+    row sample (all rows up to 2048) is compared with the oracle."""
+    note(f"case: act full config {cfg}")
+    wl = gen.make_workload(cfg, with_weights=False)
+    q, s = run_act(w, wl)
+    rows = np.arange(wl.M) if wl.M <= 2048 else _sample_rows(wl.M, 1024, cfg)
+    dec = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
+    st = parity.compare_quant(q[rows], s[rows], dec, label=f"config {cfg}")
+    note(f"  {st}")
+
+
+@pytest.mark.parametrize("a", gen.SWEEP_A)
+def test_act_shared_factor_sweep(w, a):
+    note(f"case: act sweep a={a} (config 5 shape)")
+    wl = gen.make_workload(5, a=a, with_weights=False)
+    q, s = run_act(w, wl)
+    rows = _sample_rows(wl.M, 256, 100 + a)
+    dec = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
+    st = parity.compare_quant(q[rows], s[rows], dec, label=f"sweep a={a}")
+    note(f"  {st}")
+
+
+# --------------------------------------------------------------- weight side
+
+
+@pytest.mark.parametrize("clip", [True, False])
+def test_weight_prep_tiny(w, clip):
+    note(f"case: weight prep tiny clip={clip}")
+    wl = gen.make_workload(1)
+    q, s = run_weight(w, wl, clip=clip)
+    dec = ob.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha if clip else None, wl.wbeta if clip else None)
+    parity.compare_quant(q, s, dec, label=f"weight tiny clip={clip}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_weight_prep_full_config(w, cfg):
+    note(f"case: weight prep full config {cfg}")
+    wl = gen.make_workload(cfg)
+    q, s = run_weight(w, wl)
+    rows = _sample_rows(wl.N, 512, 7 + cfg)
+    dec = ob.weight_prep(wl.W_bits[rows], wl.A, wl.B, wl.walpha[rows], wl.wbeta[rows])
+    st = parity.compare_quant(q[rows], s[rows], dec, label=f"weight config {cfg}")
+    note(f"  {st}")
+
+
+# ---------------------------------------------------------------------- GEMM
+
+
+def _rand_mx(rng, rows, K, lo=110, hi=135):
+    codes = rng.integers(0, 16, size=(rows, K), dtype=np.uint8)
+    scales = rng.integers(lo, hi, size=(rows, K // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def run_gemm(w, xc, xs, wc, ws, dtype):
+    Y = w.mxfp4_gemm(torch.from_numpy(ob.pack_codes(xc)).to(DEV), torch.from_numpy(xs).to(DEV),
+                     torch.from_numpy(ob.pack_codes(wc)).to(DEV), torch.from_numpy(ws).to(DEV), out_dtype=dtype)
+    torch.cuda.synchronize()
+    return Y.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 16, 64), (33, 47, 96), (128, 128, 256), (130, 250, 288),
+                                   (200, 64, 1024), (64, 300, 4096)])
+def test_gemm_isolated_matches_oracle(w, M, N, K):
+    """The same packed operands go to both sides (random codes and scales)."""
+    note(f"case: gemm isolated {M}x{N}x{K}")
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    xc, xs = _rand_mx(rng, M, K)
+    wc, ws = _rand_mx(rng, N, K)
+    ref = ob.gemm(xc, xs, wc, ws)
+    bound = parity.gemm_bound(ob.gemm_abs(xc, xs, wc, ws), K)
+    y32 = run_gemm(w, xc, xs, wc, ws, torch.float32)
+    err = np.abs(y32 - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert err.max() <= 1e-3 * np.abs(ref).max()
+    yb = run_gemm(w, xc, xs, wc, ws, torch.bfloat16)
+    assert np.array_equal(yb, parity.bf16_rne(y32).astype(np.float64))
+
+
+def test_gemm_exact_on_tiny_chain(w):
+    """Tiny operands from the oracle chain: fp32 accumulation of these small
+    dyadic products is exact, so the GPU result equals the exact rational sum."""
+    note("case: gemm tiny chain exact")
+    wl = gen.make_workload(1)
+    x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    wt = ob.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha, wl.wbeta)
+    ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
+    y32 = run_gemm(w, x.codes, x.scales, wt.codes, wt.scales, torch.float32)
+    bound = parity.gemm_bound(ob.gemm_abs(x.codes, x.scales, wt.codes, wt.scales), wl.K)
+    assert np.all(np.abs(y32 - ref) <= bound)
+
+
+def test_end_to_end_tiny(w):
+    note("case: end-to-end tiny")
+    wl = gen.make_workload(1)
+    xq, xs = w.act_transform_quant(dev_bf16(wl.X_bits), dev_f32(wl.A), dev_f32(wl.B),
+                                   dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta)))
+    wq, ws = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    Y = w.mxfp4_gemm(xq, xs, wq, ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    wt = ob.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha, wl.wbeta)
+    ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
+    y = Y.cpu().numpy().astype(np.float64)
+    assert np.abs(y - ref).max() <= 1e-3 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_end_to_end_full_config(w, cfg):
+    """Full-size chain X, W -> Y in the launch configuration the benchmark times;
+    sampled outputs against the oracle chain computed one row/column at a time."""
+    note(f"case: end-to-end full config {cfg}")
+    wl = gen.make_workload(cfg)
+    xq, xs = w.act_transform_quant(dev_bf16(wl.X_bits), dev_f32(wl.A), dev_f32(wl.B),
+                                   dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta)))
+    wq, ws = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    Y32 = w.mxfp4_gemm(xq, xs, wq, ws, out_dtype=torch.float32)
+    Yb = w.mxfp4_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl.M, 48, 500 + cfg)
+    cols = _sample_rows(wl.N, 48, 600 + cfg)
+    x = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
+    wt = ob.weight_prep(wl.W_bits[cols], wl.A, wl.B, wl.walpha[cols], wl.wbeta[cols])
+    ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
+    y32 = Y32[rows][:, cols].cpu().numpy().astype(np.float64)
+    rel = np.abs(y32 - ref).max() / np.abs(ref).max()
+    note(f"  max rel err {rel:.3e}")
+    assert rel <= 1e-3
+    # isolated GEMM on the GPU's own operands: elementwise fp32 bound
+    gx = ob.unpack_codes(xq[rows].cpu().numpy())
+    gw = ob.unpack_codes(wq[cols].cpu().numpy())
+    gxs, gws = xs[rows].cpu().numpy(), ws[cols].cpu().numpy()
+    ref_g, abs_g = ob.gemm_rows_cols(gx, gxs, gw, gws, np.arange(len(rows)), np.arange(len(cols)))
+    assert np.all(np.abs(y32 - ref_g) <= parity.gemm_bound(abs_g, wl.K))
+    yb = Yb[rows][:, cols].float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(yb, parity.bf16_rne(y32).astype(np.float64))

@@ -1,0 +1,18 @@
+"""BATQuant W4A4 deployment path on MI355X (gfx950).
+
+The compute lives in ``libbatq.so`` (hand-written HIP kernels behind the C ABI
+declared in ``include/batq.h``); :mod:`w4a4_bit_gemm_amd.binding` marshals
+PyTorch device tensors and streams to it.  There is no fallback: importing the
+binding raises if the library has not been built.
+"""
+from .binding import (  # noqa: F401
+    BatqError,
+    abi_version,
+    act_transform_quant,
+    clip_ratios,
+    gpk_invert,
+    library_path,
+    mxfp4_gemm,
+    prepare_weight,
+    weight_prep,
+)

@@ -1,0 +1,54 @@
+// Shared device helpers for the gfx950 kernels of the BATQuant W4A4 path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace batq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+}  // namespace batq
+
+// Host-side launchers (defined next to their kernels).
+namespace batq {
+struct TransformQuantArgs {
+  const uint16_t* x;    // [rows][ldx] bf16
+  int64_t ldx;
+  int64_t rows;
+  int64_t K;
+  int a_log2;           // shared factor size a = 1 << a_log2, private size 32 / a
+  const float* A;       // [a][a]
+  const float* B;       // [K/32][b][b]
+  const float* r_hi;    // clip ratios or nullptr (no clipping)
+  const float* r_lo;
+  int64_t r_ld;         // ratio index = row * r_ld + block (0: shared over rows)
+  uint8_t* q;           // [rows][K/2]
+  uint8_t* s;           // [rows][K/32]
+};
+hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream);
+
+struct GemmArgs {
+  const uint8_t* xq;
+  const uint8_t* xs;
+  const uint8_t* wq;
+  const uint8_t* ws;
+  int64_t M, N, K;
+  void* y;
+  int out_f32;
+};
+hipError_t launch_mxfp4_gemm(const GemmArgs& args, hipStream_t stream);
+}  // namespace batq
