@@ -236,7 +236,8 @@ def run_gemm(w, xc, xs, wc, ws, dtype):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 16, 64), (33, 47, 96), (128, 128, 256), (130, 250, 288),
-                                   (200, 64, 1024), (64, 300, 4096)])
+                                   (200, 64, 1024), (64, 300, 4096), (33, 47, 512), (257, 129, 768),
+                                   (512, 512, 2048)])
 def test_gemm_isolated_matches_oracle(w, M, N, K):
     """The same packed operands go to both sides (random codes and scales)."""
     note(f"case: gemm isolated {M}x{N}x{K}")

@@ -170,6 +170,7 @@ batq_status batq_mxfp4_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
   args.K = K;
   args.y = Y;
   args.out_f32 = (out == BATQ_OUT_F32);
+  args.vec_store = aligned(Y, 16) && (N % (args.out_f32 ? 4 : 8) == 0);
   return batq::launch_mxfp4_gemm(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 

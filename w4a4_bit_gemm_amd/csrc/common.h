@@ -49,6 +49,7 @@ struct GemmArgs {
   int64_t M, N, K;
   void* y;
   int out_f32;
+  int vec_store;  // Y 16-byte aligned and rows a whole number of 16-byte chunks
 };
 hipError_t launch_mxfp4_gemm(const GemmArgs& args, hipStream_t stream);
 }  // namespace batq
