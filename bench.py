@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--a", type=int, default=8, help="shared factor size (config 5 sweep)")
+    ap.add_argument("--gemm", choices=["packed", "unpacked"], default="packed",
+                    help="weight operand layout of the GEMM (packed: lane-ordered, prepared offline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="token rows in the oracle sample")
     ap.add_argument("--cpu-cols", type=int, default=2048, help="weight rows in the oracle sample")
@@ -130,6 +132,8 @@ def main():
     rh = f32(w.clip_ratios(wl.alpha))
     rl = f32(w.clip_ratios(wl.beta))
     Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)  # offline
+    packed = args.gemm == "packed"
+    Wp0 = w.weight_pack(Wq0, Ws0) if packed else None  # offline
     torch.cuda.synchronize()
 
     set_bytes = M * K * 2 + M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
@@ -138,7 +142,9 @@ def main():
     sets = []
     for _ in range(nsets):
         sets.append(dict(
-            X=X0.clone(), Wq=Wq0.clone(), Ws=Ws0.clone(),
+            X=X0.clone(),
+            Wq=None if packed else Wq0.clone(), Ws=None if packed else Ws0.clone(),
+            Wp=w.PackedWeight(Wp0.data.clone(), N, K) if packed else None,
             Xq=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
             Xs=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
             Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
@@ -151,7 +157,10 @@ def main():
         w.act_transform_quant(s["X"], A, B, rh, rl, out=(s["Xq"], s["Xs"]))
         if ev is not None:
             ev[1].record()
-        w.mxfp4_gemm(s["Xq"], s["Xs"], s["Wq"], s["Ws"], out=s["Y"])
+        if packed:
+            w.mxfp4_gemm_packed(s["Xq"], s["Xs"], s["Wp"], out=s["Y"])
+        else:
+            w.mxfp4_gemm(s["Xq"], s["Xs"], s["Wq"], s["Ws"], out=s["Y"])
         if ev is not None:
             ev[2].record()
 
@@ -193,9 +202,11 @@ def main():
                 "frac": act_gbs / HBM_PEAK_GBS}
     dominant_is_gemm = t_gemm.mean() >= t_act.mean()
     roof = dict(gemm_roof if dominant_is_gemm else act_roof)
-    traffic = load_traffic("mxfp4_gemm.hip" if dominant_is_gemm else "transform_quant.hip")
+    gemm_src = "mxfp4_gemm_packed.hip" if packed else "mxfp4_gemm.hip"
+    gemm_kernel = "mxfp4_gemm_packed_kernel" if packed else "mxfp4_gemm_dma_kernel"
+    traffic = load_traffic(gemm_src if dominant_is_gemm else "transform_quant.hip")
     roof["traffic"] = traffic
-    roof["kernel"] = "mxfp4_gemm_kernel" if dominant_is_gemm else "transform_quant_kernel"
+    roof["kernel"] = gemm_kernel if dominant_is_gemm else "transform_quant_kernel"
     act_roof["traffic"] = load_traffic("transform_quant.hip")
 
     out = {
@@ -213,16 +224,16 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), "
-                        f"W {N}x{K} bf16 N(0,0.02) pre-packed offline; GPK a={wl.a} b={wl.b}; "
+                        f"W {N}x{K} bf16 N(0,0.02) prepared offline ({args.gemm} MXFP4); GPK a={wl.a} b={wl.b}; "
                         f"step = act transform+clip+MXFP4 quant + MXFP4 GEMM (bf16 out)",
-            "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets,
+            "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets, "gemm": args.gemm,
         },
         "roofline": roof,
         "kernels": {
             "transform_quant": {"us": float(t_act.mean() * 1e6), "GB/s": act_gbs,
                                 "frac_hbm": act_gbs / HBM_PEAK_GBS, "algorithmic_bytes": act_bytes,
                                 "roofline": act_roof},
-            "mxfp4_gemm": {"us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
+            "mxfp4_gemm": {"kernel": gemm_kernel, "us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
                            "frac_mfma": gemm_tflops / MXFP4_PEAK_TFLOPS, "flops": flops,
                            "operand_output_bytes": gemm_bytes},
         },

@@ -136,6 +136,36 @@ batq_status batq_mxfp4_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
                             const uint8_t* Ws, int64_t M, int64_t N, int64_t K, void* Y,
                             batq_out_dtype out, hipStream_t stream);
 
+/* ------------------------------------------------- packed-weight fast path
+ * The weight side is fixed after the offline step, so it can also be stored
+ * in the order the matrix cores consume it.  The packed GEMM computes exactly
+ * the same sums, in the same order, as batq_mxfp4_gemm; it needs K % 256 == 0.
+ */
+
+/* Bytes of the packed form of an [N][K/2] + [N][K/32] MXFP4 weight:
+ * ceil(N/32) * (K/256) * 4352.  Returns -1 for N < 0 or K not a positive
+ * multiple of 256.  Host only. */
+int64_t batq_weight_packed_bytes(int64_t N, int64_t K);
+
+/* Offline: repack Wq/Ws (batq_weight_prep outputs) for batq_mxfp4_gemm_packed.
+ * Layout, per group of 32 rows n32 and 256-k stage s (4352 bytes): four
+ * sub-steps j of 64 lanes x 16 code bytes (lane l: MX block 8s + 4(l/32) + j of
+ * row 32 n32 + l%32), then 64 lanes x 4 scale bytes (lane l: blocks
+ * 8s + 4(l/32) + 0..3 of the same row).  Rows past N are zero codes with unit
+ * scale.  Wp: batq_weight_packed_bytes(N, K) bytes, 16-byte aligned.
+ * Wq 16-byte aligned.  N == 0 is a no-op.
+ * Errors: NULL, SHAPE (K % 256 != 0), ALIGN, HIP. */
+batq_status batq_weight_pack(const uint8_t* Wq, const uint8_t* Ws, int64_t N, int64_t K, uint8_t* Wp,
+                             hipStream_t stream);
+
+/* Y[M][N] = deq(Xq,Xs) deq(W)^T with W given packed by batq_weight_pack; same
+ * result as batq_mxfp4_gemm on the unpacked operands [en.papernotes.org, Key
+ * Designs §1 and §4].  Xq 16-byte aligned, Xs 4-byte aligned, Wp 16-byte
+ * aligned, Y 4-byte aligned.  M == 0 or N == 0 is a no-op.
+ * Errors: NULL, SHAPE (K % 256 != 0), ALIGN, UNSUPPORTED (output type), HIP. */
+batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wp, int64_t M,
+                                   int64_t N, int64_t K, void* Y, batq_out_dtype out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

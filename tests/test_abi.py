@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("batq_act_transform_quant", "batq_weight_prep", "batq_mxfp4_gemm", "batq_gpk_invert",
-              "batq_clip_ratios", "batq_abi_version", "batq_status_str"):
+              "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
+              "batq_weight_pack", "batq_mxfp4_gemm_packed"):
         assert n in names
 
 
@@ -85,6 +86,41 @@ def test_gemm_argument_checks(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, FAKE + 2, 0, None) == ALIGN
     assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, FAKE, 0, None) == OK
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, FAKE, 1, None) == OK
+
+
+def test_packed_size(lib):
+    f = lib.batq_weight_packed_bytes
+    assert f(12288, 4096) == 384 * 16 * 4352
+    assert f(33, 512) == 2 * 2 * 4352
+    assert f(0, 256) == 0
+    assert f(4, 100) == -1 and f(4, 0) == -1 and f(-1, 256) == -1 and f(4, 288) == -1
+
+
+def test_pack_argument_checks(lib):
+    f = lib.batq_weight_pack
+    assert f(FAKE, FAKE, 4, 288, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, -1, 256, FAKE, None) == SHAPE
+    assert f(0, FAKE, 4, 256, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 4, 256, 0, None) == NULL
+    assert f(FAKE + 8, FAKE, 4, 256, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, 4, 256, FAKE + 4, None) == ALIGN
+    assert f(FAKE, FAKE, 0, 256, FAKE, None) == OK
+
+
+def test_packed_gemm_argument_checks(lib):
+    f = lib.batq_mxfp4_gemm_packed
+    assert f(FAKE, FAKE, FAKE, 4, 4, 288, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, -1, 256, FAKE, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 4, 256, FAKE, 3, None) == UNSUP
+    assert f(FAKE, 0, FAKE, 4, 4, 256, FAKE, 0, None) == NULL
+    assert f(FAKE, FAKE, 0, 4, 4, 256, FAKE, 0, None) == NULL
+    assert f(FAKE + 8, FAKE, FAKE, 4, 4, 256, FAKE, 0, None) == ALIGN
+    assert f(FAKE, FAKE + 2, FAKE, 4, 4, 256, FAKE, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE + 4, 4, 4, 256, FAKE, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, 4, 256, FAKE + 2, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 0, 4, 256, FAKE, 0, None) == OK
+    assert f(FAKE, FAKE, FAKE, 4, 0, 256, FAKE, 1, None) == OK
 
 
 def test_clip_ratios_match_oracle():

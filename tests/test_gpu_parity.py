@@ -311,3 +311,112 @@ def test_end_to_end_full_config(w, cfg):
     assert np.all(np.abs(y32 - ref_g) <= parity.gemm_bound(abs_g, wl.K))
     yb = Yb[rows][:, cols].float().cpu().numpy().astype(np.float64)
     assert np.array_equal(yb, parity.bf16_rne(y32).astype(np.float64))
+
+
+# ------------------------------------------------------- packed-weight GEMM
+
+
+def _packed_layout(wq_bytes: np.ndarray, ws: np.ndarray) -> np.ndarray:
+    """The byte layout batq_weight_pack documents, written out with numpy."""
+    N, K2 = wq_bytes.shape
+    K = 2 * K2
+    G, S = (N + 31) // 32, K // 256
+    codes = np.zeros((G * 32, K2), np.uint8)
+    codes[:N] = wq_bytes
+    scales = np.full((G * 32, K // 32), 127, np.uint8)
+    scales[:N] = ws
+    out = np.zeros((G, S, 4352), np.uint8)
+    lanes = np.arange(64)
+    for g in range(G):
+        rows = 32 * g + lanes % 32
+        for s in range(S):
+            first = 8 * s + 4 * (lanes // 32)  # MX block of sub-step 0, per lane
+            for j in range(4):
+                blk = first + j
+                out[g, s, 1024 * j:1024 * (j + 1)] = np.stack(
+                    [codes[rows[l], 16 * blk[l]:16 * blk[l] + 16] for l in range(64)]).reshape(-1)
+            out[g, s, 4096:] = np.stack([scales[rows[l], first[l]:first[l] + 4] for l in range(64)]).reshape(-1)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (32, 512), (47, 768), (300, 256)])
+def test_weight_pack_layout(w, N, K):
+    note(f"case: weight pack layout {N}x{K}")
+    rng = np.random.default_rng(N + K)
+    wc, ws = _rand_mx(rng, N, K)
+    wq = ob.pack_codes(wc)
+    P = w.weight_pack(torch.from_numpy(wq).to(DEV), torch.from_numpy(ws).to(DEV))
+    torch.cuda.synchronize()
+    got = P.data.cpu().numpy()
+    assert got.size == w.weight_packed_bytes(N, K)
+    assert np.array_equal(got, _packed_layout(wq, ws))
+
+
+def run_gemm_packed(w, xc, xs, wc, ws, dtype):
+    wp = w.weight_pack(torch.from_numpy(ob.pack_codes(wc)).to(DEV), torch.from_numpy(ws).to(DEV))
+    Y = w.mxfp4_gemm_packed(torch.from_numpy(ob.pack_codes(xc)).to(DEV), torch.from_numpy(xs).to(DEV), wp,
+                            out_dtype=dtype)
+    torch.cuda.synchronize()
+    return Y.float().cpu().numpy().astype(np.float64)
+
+
+# K / 256 in {1, 2, 4, 8, 16, 48} take the fully unrolled kernels; 3, 6, 12 the
+# looped one.  M and N cover partial row and column tiles.
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (33, 47, 256), (128, 256, 512), (130, 250, 768),
+                                   (257, 129, 1024), (40, 33, 1536), (200, 300, 2048), (64, 520, 3072),
+                                   (64, 300, 4096), (129, 257, 12288)])
+def test_packed_gemm_matches_oracle_and_unpacked(w, M, N, K):
+    note(f"case: packed gemm {M}x{N}x{K}")
+    rng = np.random.default_rng(M * 5 + N * 11 + K)
+    xc, xs = _rand_mx(rng, M, K)
+    wc, ws = _rand_mx(rng, N, K)
+    ref = ob.gemm(xc, xs, wc, ws)
+    bound = parity.gemm_bound(ob.gemm_abs(xc, xs, wc, ws), K)
+    y32 = run_gemm_packed(w, xc, xs, wc, ws, torch.float32)
+    err = np.abs(y32 - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+    # same MFMA sequence per output as the unpacked kernel: identical bits
+    assert np.array_equal(y32, run_gemm(w, xc, xs, wc, ws, torch.float32))
+    yb = run_gemm_packed(w, xc, xs, wc, ws, torch.bfloat16)
+    assert np.array_equal(yb, parity.bf16_rne(y32).astype(np.float64))
+
+
+def test_packed_gemm_unaligned_output(w):
+    """Y rows not a whole number of 16-byte chunks: scalar store path."""
+    note("case: packed gemm unaligned output")
+    rng = np.random.default_rng(77)
+    M, N, K = 70, 61, 512
+    xc, xs = _rand_mx(rng, M, K)
+    wc, ws = _rand_mx(rng, N, K)
+    ref = ob.gemm(xc, xs, wc, ws)
+    bound = parity.gemm_bound(ob.gemm_abs(xc, xs, wc, ws), K)
+    for dt in (torch.float32, torch.bfloat16):
+        y = run_gemm_packed(w, xc, xs, wc, ws, dt)
+        lim = bound if dt == torch.float32 else bound + np.abs(ref) * 2.0 ** -8
+        assert np.all(np.abs(y - ref) <= lim)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_packed_end_to_end_full_config(w, cfg):
+    """The chain the benchmark times (prepared weight packed offline): equal to
+    the unpacked GEMM on the same operands, bit for bit, over the whole output;
+    the unpacked path is held to the oracle by the tests above."""
+    note(f"case: packed end-to-end config {cfg}")
+    wl = gen.make_workload(cfg)
+    xq, xs = w.act_transform_quant(dev_bf16(wl.X_bits), dev_f32(wl.A), dev_f32(wl.B),
+                                   dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta)))
+    wq, ws = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    wp = w.weight_pack(wq, ws)
+    Yp = w.mxfp4_gemm_packed(xq, xs, wp, out_dtype=torch.bfloat16)
+    Yu = w.mxfp4_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(Yp, Yu)
+    rows = _sample_rows(wl.M, 16, 700 + cfg)
+    cols = _sample_rows(wl.N, 16, 800 + cfg)
+    x = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
+    wt = ob.weight_prep(wl.W_bits[cols], wl.A, wl.B, wl.walpha[cols], wl.wbeta[cols])
+    ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
+    y = Yp[rows][:, cols].float().cpu().numpy().astype(np.float64)
+    rel = np.abs(y - ref).max() / np.abs(ref).max()
+    note(f"  max rel err {rel:.3e}")
+    assert rel <= 1e-2  # bf16 output rounding on top of the fp32 bound

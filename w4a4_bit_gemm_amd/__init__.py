@@ -13,6 +13,10 @@ from .binding import (  # noqa: F401
     gpk_invert,
     library_path,
     mxfp4_gemm,
+    mxfp4_gemm_packed,
+    PackedWeight,
+    weight_pack,
+    weight_packed_bytes,
     prepare_weight,
     weight_prep,
 )

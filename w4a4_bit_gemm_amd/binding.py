@@ -56,6 +56,12 @@ def _load():
     lib.batq_weight_prep.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, P, P]
     lib.batq_mxfp4_gemm.restype = ctypes.c_int
     lib.batq_mxfp4_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    lib.batq_weight_packed_bytes.restype = I64
+    lib.batq_weight_packed_bytes.argtypes = [I64, I64]
+    lib.batq_weight_pack.restype = ctypes.c_int
+    lib.batq_weight_pack.argtypes = [P, P, I64, I64, P, P]
+    lib.batq_mxfp4_gemm_packed.restype = ctypes.c_int
+    lib.batq_mxfp4_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
     _lib = lib
     return lib
 
@@ -215,5 +221,60 @@ def mxfp4_gemm(Xq, Xs, Wq, Ws, out_dtype=None, out=None):
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
     st = _load().batq_mxfp4_gemm(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, _ptr(out), code,
                                  _stream_ptr(torch, Xq.device))
+    _check(st)
+    return out
+
+
+def weight_packed_bytes(N: int, K: int) -> int:
+    """Bytes of the packed weight form (C ABI; -1 for unsupported shapes)."""
+    return int(_load().batq_weight_packed_bytes(N, K))
+
+
+class PackedWeight:
+    """A weight in the matrix-core lane order produced by :func:`weight_pack`."""
+
+    def __init__(self, data, N: int, K: int):
+        self.data = data
+        self.N = N
+        self.K = K
+
+
+def weight_pack(Wq, Ws, out=None) -> PackedWeight:
+    """Offline: repack MXFP4 weights (from :func:`weight_prep`) for
+    :func:`mxfp4_gemm_packed`.  Needs K % 256 == 0."""
+    torch = _torch()
+    _req(Wq, torch.uint8, "Wq")
+    _req(Ws, torch.uint8, "Ws")
+    N, K2 = Wq.shape
+    K = 2 * K2
+    nbytes = weight_packed_bytes(N, K)
+    if nbytes < 0:
+        raise ValueError("packed weights need K to be a positive multiple of 256")
+    if out is None:
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=Wq.device)
+    _check(_load().batq_weight_pack(_ptr(Wq), _ptr(Ws), N, K, _ptr(out), _stream_ptr(torch, Wq.device)))
+    return PackedWeight(out, N, K)
+
+
+def mxfp4_gemm_packed(Xq, Xs, Wp: PackedWeight, out_dtype=None, out=None):
+    """Y = deq(Xq, Xs) deq(W)^T with W packed by :func:`weight_pack`; same
+    result as :func:`mxfp4_gemm` on the unpacked weight."""
+    torch = _torch()
+    _req(Xq, torch.uint8, "Xq")
+    _req(Xs, torch.uint8, "Xs")
+    M, K2 = Xq.shape
+    K = 2 * K2
+    if K != Wp.K or tuple(Xs.shape) != (M, K // 32):
+        raise ValueError("operand shapes do not match")
+    N = Wp.N
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
+    else:
+        _req(out, out_dtype, "out")
+    code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    st = _load().batq_mxfp4_gemm_packed(_ptr(Xq), _ptr(Xs), _ptr(Wp.data), M, N, K, _ptr(out), code,
+                                        _stream_ptr(torch, Xq.device))
     _check(st)
     return out

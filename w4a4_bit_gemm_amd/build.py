@@ -21,6 +21,8 @@ HIPCC_FLAGS = [
     # packed FP32 math stays off (the compiler would otherwise emit v_pk_* ops)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # the GEMM kernels fully unroll their stage loops for common K (exact wait counts)
+    "-mllvm", "-pragma-unroll-threshold=1000000",
 ]
 
 

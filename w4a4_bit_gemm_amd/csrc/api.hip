@@ -174,4 +174,39 @@ batq_status batq_mxfp4_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t*
   return batq::launch_mxfp4_gemm(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 
+int64_t batq_weight_packed_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K % 256 != 0) return -1;
+  return batq::packed_weight_bytes(N, K);
+}
+
+batq_status batq_weight_pack(const uint8_t* Wq, const uint8_t* Ws, int64_t N, int64_t K, uint8_t* Wp,
+                             hipStream_t stream) {
+  if (N < 0 || K <= 0 || K % 256 != 0) return BATQ_ERR_SHAPE;
+  if (Wq == nullptr || Ws == nullptr || Wp == nullptr) return BATQ_ERR_NULL;
+  if (!aligned(Wq, 16) || !aligned(Wp, 16)) return BATQ_ERR_ALIGN;
+  if (N == 0) return BATQ_OK;
+  return batq::launch_weight_pack(Wq, Ws, N, K, Wp, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
+}
+
+batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wp, int64_t M,
+                                   int64_t N, int64_t K, void* Y, batq_out_dtype out, hipStream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 256 != 0) return BATQ_ERR_SHAPE;
+  if (out != BATQ_OUT_BF16 && out != BATQ_OUT_F32) return BATQ_ERR_UNSUPPORTED;
+  if (Xq == nullptr || Xs == nullptr || Wp == nullptr || Y == nullptr) return BATQ_ERR_NULL;
+  if (!aligned(Xq, 16) || !aligned(Xs, 4) || !aligned(Wp, 16) || !aligned(Y, 4)) return BATQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return BATQ_OK;
+  batq::GemmArgs args;
+  args.xq = Xq;
+  args.xs = Xs;
+  args.wq = Wp;
+  args.ws = nullptr;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.y = Y;
+  args.out_f32 = (out == BATQ_OUT_F32);
+  args.vec_store = aligned(Y, 16) && (N % (args.out_f32 ? 4 : 8) == 0);
+  return batq::launch_mxfp4_gemm_packed(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
+}
+
 }  // extern "C"

@@ -52,4 +52,14 @@ struct GemmArgs {
   int vec_store;  // Y 16-byte aligned and rows a whole number of 16-byte chunks
 };
 hipError_t launch_mxfp4_gemm(const GemmArgs& args, hipStream_t stream);
+
+// Packed weight layout for the GEMM's B operand (see mxfp4_gemm.hip):
+// per 32-row group and 256-k stage, 4 x 64 lanes x 16 code bytes followed by
+// 64 lanes x 4 scale bytes.
+constexpr int64_t kPackGroupBytes = 4 * 64 * 16 + 64 * 4;
+inline int64_t packed_weight_bytes(int64_t N, int64_t K) { return ((N + 31) / 32) * (K / 256) * kPackGroupBytes; }
+hipError_t launch_weight_pack(const uint8_t* wq, const uint8_t* ws, int64_t N, int64_t K, uint8_t* wp,
+                              hipStream_t stream);
+// Same GemmArgs; wq points at the packed buffer and ws is unused.
+hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream);
 }  // namespace batq

@@ -1,0 +1,392 @@
+// W4A4 GEMM with the weight operand in a packed, MFMA-lane-ordered layout.
+//
+// Same product and accumulation order as the canonical GEMM [BATQuant note
+// (en.papernotes.org), Key Designs §1 and §4], for weights that were packed
+// once, offline, after batq_weight_prep.  Packing matters because on gfx950
+// the canonical kernel is bound by LDS traffic: every operand byte is written
+// to and read back from LDS.  With the weights in lane order, each wave loads
+// its weight fragments with fully coalesced 1 KB instructions straight into
+// registers, and only the activation tile (shared by the four waves) goes
+// through LDS, which cuts LDS bytes per MFMA roughly in half.
+//
+// Packed layout, per group of 32 weight rows (n32) and per 256-k stage (s),
+// 4352 bytes:
+//   codes: 4 sub-steps j x 64 lanes x 16 bytes.  Lane l = (r, g), r = l % 32,
+//          g = l / 32, holds MX block 8 s + 4 g + j of row 32 n32 + r.
+//   scales: 64 lanes x 4 bytes: lane l holds the scale bytes of blocks
+//          8 s + 4 g + 0..3 of row 32 n32 + r (byte j = block 8 s + 4 g + j).
+// Rows past N are zero codes with unit scales.
+//
+// Kernel: workgroup tile 128 (M) x 256 (N); wave w owns all 128 rows and
+// columns 64 w .. 64 w + 63 (4 x 2 MFMA tiles of 32 x 32).  Activations: a
+// three-slot direct-to-LDS ring (16 KB codes + 1 KB scales per stage).
+// Weights: three register sets (stages s, s+1, s+2 in flight).
+#include "common.h"
+
+namespace batq {
+
+namespace {
+
+constexpr int kMT = 4;         // 32-row A tiles per wave
+constexpr int kNT = 2;         // 32-column B tiles per wave
+constexpr int kBM = 32 * kMT;  // 128
+constexpr int kBN = 4 * 32 * kNT;  // 256, four waves along N
+constexpr int kRowBytes = 128;
+constexpr int kAStage = kBM * kRowBytes;        // 16 KB
+constexpr int kAScale = kBM * 8;                // 1 KB
+constexpr int kSlot = kAStage + kAScale;
+constexpr int kEpiStride = 32 * kNT + 8;        // floats
+constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes
+
+__device__ __forceinline__ i32x8 op(uint4 v) {
+  i32x8 r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  return r;
+}
+
+template <int J>
+__device__ __forceinline__ f32x16 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb, f32x16 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(a), op(b), acc, 4, 4, J, (int)sa, J, (int)sb);
+}
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// ------------------------------------------------------------------ packing
+
+__global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t* __restrict__ wq,
+                                                          const uint8_t* __restrict__ ws, int64_t N, int64_t K,
+                                                          uint8_t* __restrict__ wp) {
+  const int64_t nst = K / 256;
+  const int64_t groups = ((N + 31) / 32) * nst;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // one (n32, s) per wave
+  if (item >= groups) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t n32 = item / nst;
+  const int64_t s = item % nst;
+  const int64_t row = 32 * n32 + (lane & 31);
+  const int g = lane >> 5;
+  uint8_t* dst = wp + item * kPackGroupBytes;
+  uint32_t sc = 0x7F7F7F7Fu;
+  uint4 c[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if (row < N) {
+    const uint8_t* qr = wq + row * (K / 2) + 16 * (8 * s + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = *reinterpret_cast<const uint4*>(qr + 16 * j);
+    const uint8_t* sr = ws + row * (K / 32) + 8 * s + 4 * g;
+    sc = (uint32_t)sr[0] | (uint32_t)sr[1] << 8 | (uint32_t)sr[2] << 16 | (uint32_t)sr[3] << 24;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + j * 1024 + 16 * lane) = c[j];
+  *reinterpret_cast<uint32_t*>(dst + 4096 + 4 * lane) = sc;
+}
+
+// -------------------------------------------------------------------- GEMM
+
+// Register sets are plain named variables (declared by the macros below): an
+// aggregate (array or vector type) either reaches the early alloca passes
+// with loop-variable indices and lands in scratch, or forces whole-aggregate
+// live ranges that the allocator cannot split.  kNT == 2 is assumed.
+static_assert(kNT == 2, "weight register sets below hold two 32-column tiles");
+
+// Stage index laundered through an empty asm: the address arithmetic that
+// depends on it cannot be hoisted out of its pipeline step, so fully unrolled
+// kernels do not keep every stage's addresses live at once.
+__device__ __forceinline__ int64_t opaque_stage(int64_t s) {
+  asm volatile("" : "+s"(s));
+  return s;
+}
+
+__device__ __forceinline__ const uint8_t* b_src(const uint8_t* wp, int64_t n32, int64_t nst, int64_t s) {
+  return wp + (n32 * nst + s) * kPackGroupBytes;
+}
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+#define BATQ_DECL_B(n) \
+  uint4 n##_00, n##_01, n##_02, n##_03, n##_10, n##_11, n##_12, n##_13; \
+  uint32_t n##_s0, n##_s1;
+// weight stage ST of this wave's two 32-row groups -> set n
+#define BATQ_LOAD_B(n, ST)                                                                     \
+  {                                                                                            \
+    const int64_t off_ = opaque_stage(ST) * kPackGroupBytes;                                   \
+    const uint8_t* s0_ = b_base0 + off_;                                                       \
+    const uint8_t* s1_ = b_base1 + off_;                                                       \
+    n##_00 = ld16(s0_); n##_01 = ld16(s0_ + 1024); n##_02 = ld16(s0_ + 2048); n##_03 = ld16(s0_ + 3072); \
+    n##_s0 = ld4(s0_ + 4096 - 12 * lane);                                                      \
+    n##_10 = ld16(s1_); n##_11 = ld16(s1_ + 1024); n##_12 = ld16(s1_ + 2048); n##_13 = ld16(s1_ + 3072); \
+    n##_s1 = ld4(s1_ + 4096 - 12 * lane);                                                      \
+  }
+#define BATQ_DECL_A(n) uint4 n##_0, n##_1, n##_2, n##_3; uint32_t n##_s;
+// activation stage ST -> set n: thread owns code chunks id = tid + 256 i
+// (row id / 8, chunk id % 8) and scale dword (row tid / 2, half tid % 2)
+#define BATQ_LOAD_A(n, ST)                                                                     \
+  {                                                                                            \
+    const int64_t st_ = opaque_stage(ST);                                                      \
+    const int64_t off_ = st_ * kRowBytes;                                                      \
+    n##_0 = ld16(a_base0 + off_);                                                              \
+    n##_1 = ld16(a_base1 + off_);                                                              \
+    n##_2 = ld16(a_base2 + off_);                                                              \
+    n##_3 = ld16(a_base3 + off_);                                                              \
+    n##_s = ld4(a_sbase + 8 * st_);                                                            \
+  }
+#define BATQ_STORE_A(n, SLOT)                                                                  \
+  {                                                                                            \
+    a_dst(SLOT, tid)[0] = n##_0;                                                               \
+    a_dst(SLOT, tid + 256)[0] = n##_1;                                                         \
+    a_dst(SLOT, tid + 512)[0] = n##_2;                                                         \
+    a_dst(SLOT, tid + 768)[0] = n##_3;                                                         \
+    *reinterpret_cast<uint32_t*>((SLOT) + kAStage + 4 * tid) = n##_s;                          \
+  }
+
+// Stage-invariant per-thread source pointers (row clamped: rows past the edge
+// read a valid row and are never stored).
+__device__ __forceinline__ const uint8_t* a_row_base(const GemmArgs& p, int64_t m0, int id) {
+  int64_t gr = m0 + (id >> 3);
+  gr = gr < p.M ? gr : p.M - 1;
+  return p.xq + gr * (p.K >> 1) + 16 * (id & 7);
+}
+__device__ __forceinline__ const uint8_t* a_scale_base(const GemmArgs& p, int64_t m0, int tid) {
+  int64_t gr = m0 + (tid >> 1);
+  gr = gr < p.M ? gr : p.M - 1;
+  return p.xs + gr * (p.K >> 5) + 4 * (tid & 1);
+}
+__device__ __forceinline__ uint4* a_dst(uint8_t* slot, int id) {
+  const int row = id >> 3;
+  return reinterpret_cast<uint4*>(slot + row * kRowBytes + 16 * ((id & 7) ^ swz(row)));
+}
+
+__device__ __forceinline__ uint4 lds_frag(const uint8_t* base, int row, int chunk) {
+  return *reinterpret_cast<const uint4*>(base + row * kRowBytes + 16 * (chunk ^ swz(row)));
+}
+
+template <int J>
+__device__ __forceinline__ void mma_sub(f32x16 (&acc)[kMT][kNT], const uint4 (&fa)[kMT], uint4 b0, uint4 b1,
+                                        uint32_t bs0, uint32_t bs1, const uint32_t (&sa)[kMT]) {
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    acc[i][0] = mfma_fp4<J>(fa[i], b0, sa[i], bs0, acc[i][0]);
+    acc[i][1] = mfma_fp4<J>(fa[i], b1, sa[i], bs1, acc[i][1]);
+  }
+}
+
+__device__ __forceinline__ void read_a(const uint8_t* As, int j, uint4 (&fa)[kMT], int r32, int g) {
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) fa[i] = lds_frag(As, 32 * i + r32, 4 * g + j);
+}
+
+// Stage from an LDS slot and a weight register set into the accumulators,
+// with the LDS reads of sub-step j+1 issued ahead of the MFMAs of sub-step j.
+#define BATQ_MMA_STAGE(SLOT, n)                                                                \
+  {                                                                                            \
+    uint32_t sa_[kMT];                                                                         \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i)                                            \
+      sa_[i] = ld4((SLOT) + kAStage + (32 * i + r32) * 8 + 4 * g);                             \
+    uint4 fa0_[kMT], fa1_[kMT];                                                                \
+    read_a(SLOT, 0, fa0_, r32, g);                                                             \
+    read_a(SLOT, 1, fa1_, r32, g);                                                             \
+    sched_fence();                                                                             \
+    mma_sub<0>(acc, fa0_, n##_00, n##_10, n##_s0, n##_s1, sa_);                                \
+    sched_fence();                                                                             \
+    read_a(SLOT, 2, fa0_, r32, g);                                                             \
+    sched_fence();                                                                             \
+    mma_sub<1>(acc, fa1_, n##_01, n##_11, n##_s0, n##_s1, sa_);                                \
+    sched_fence();                                                                             \
+    read_a(SLOT, 3, fa1_, r32, g);                                                             \
+    sched_fence();                                                                             \
+    mma_sub<2>(acc, fa0_, n##_02, n##_12, n##_s0, n##_s1, sa_);                                \
+    sched_fence();                                                                             \
+    mma_sub<3>(acc, fa1_, n##_03, n##_13, n##_s0, n##_s1, sa_);                                \
+  }
+
+// NST > 0: stage count fixed at compile time, loop fully unrolled (exact
+// compiler wait counts).  NST == 0: runtime stage count.
+template <int NST>
+__global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t epi_buf[4 * kEpiWave];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);  // XCD-aware order
+  const int tm = t % tiles_m;
+  const int tn = t / tiles_m;
+  const int64_t m0 = (int64_t)tm * kBM;
+  const int64_t n0 = (int64_t)tn * kBN + 64 * wave;  // this wave's first column
+  const int64_t n32_0 = n0 / 32;
+  const int64_t nst = NST > 0 ? NST : p.K / 256;
+  const int64_t last = nst - 1;
+  const int64_t n32_max = (p.N + 31) / 32;
+  // Each of the wave's two 32-column groups is clamped on its own to the last
+  // group: a clamped group is computed (so every wave reaches every barrier)
+  // but its columns lie past N and are never stored.
+  const int64_t n32_g0 = n32_0 < n32_max ? n32_0 : n32_max - 1;
+  const int64_t n32_g1 = n32_0 + 1 < n32_max ? n32_0 + 1 : n32_max - 1;
+
+  f32x16 acc[kMT][kNT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) acc[i][k] = f32x16{};
+
+  // Pipeline (all loads are plain loads into registers, so the compiler's
+  // in-order wait counts stay exact): at step s, stage s is read from LDS slot
+  // s % 2; activation stage s+1 moves registers -> the other slot; activation
+  // stage s+3 and weight stage s+2 are requested.  Stage indices of the
+  // prefetches are clamped to the last stage (a clamped load re-reads an
+  // L2-resident stage and is never used), keeping every step branch-free.
+#define BATQ_CL(x) ((x) < last ? (x) : last)
+  const uint8_t* const a_base0 = a_row_base(p, m0, tid);
+  const uint8_t* const a_base1 = a_row_base(p, m0, tid + 256);
+  const uint8_t* const a_base2 = a_row_base(p, m0, tid + 512);
+  const uint8_t* const a_base3 = a_row_base(p, m0, tid + 768);
+  const uint8_t* const a_sbase = a_scale_base(p, m0, tid);
+  const uint8_t* const b_base0 = b_src(p.wq, n32_g0, nst, 0) + 16 * lane;
+  const uint8_t* const b_base1 = b_src(p.wq, n32_g1, nst, 0) + 16 * lane;
+  BATQ_DECL_A(a0)
+  BATQ_DECL_A(a1)
+  BATQ_DECL_B(b0)
+  BATQ_DECL_B(b1)
+  BATQ_DECL_B(b2)
+  BATQ_LOAD_A(a0, 0)
+  BATQ_LOAD_B(b0, 0)
+  if (NST == 0 || NST > 1) {
+    BATQ_LOAD_A(a1, BATQ_CL(1))
+    BATQ_LOAD_B(b1, BATQ_CL(1))
+  }
+  BATQ_STORE_A(a0, slot0)
+  if (NST == 0 || NST > 2) BATQ_LOAD_A(a0, BATQ_CL(2))
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  block_barrier();
+
+  // With a compile-time stage count the tail prefetches are simply omitted
+  // (the conditions fold away); a runtime count keeps them, clamped.
+#define BATQ_STEP(S, CUR, NEXT, ANEXT, BCUR, BPF)                                               \
+  {                                                                                            \
+    if (NST == 0 || (S) + 1 < NST) BATQ_STORE_A(ANEXT, NEXT)   /* act stage s+1 -> LDS */       \
+    if (NST == 0 || (S) + 3 < NST) BATQ_LOAD_A(ANEXT, BATQ_CL((S) + 3)) /* act stage s+3 */     \
+    if (NST == 0 || (S) + 2 < NST) BATQ_LOAD_B(BPF, BATQ_CL((S) + 2))   /* weight stage s+2 */  \
+    sched_fence();                                                                             \
+    BATQ_MMA_STAGE(CUR, BCUR)                                                                  \
+    __builtin_amdgcn_s_waitcnt(0xC07F);          /* lgkmcnt(0): s+1 written, s read */         \
+    block_barrier();                                                                           \
+  }
+  // Slots alternate with period 2 and weight sets with period 3.
+#define BATQ_STEP6(S)                                                                          \
+  switch ((S) % 6) {                                                                           \
+    case 0: BATQ_STEP(S, slot0, slot1, a1, b0, b2) break;                                      \
+    case 1: BATQ_STEP(S, slot1, slot0, a0, b1, b0) break;                                      \
+    case 2: BATQ_STEP(S, slot0, slot1, a1, b2, b1) break;                                      \
+    case 3: BATQ_STEP(S, slot1, slot0, a0, b0, b2) break;                                      \
+    case 4: BATQ_STEP(S, slot0, slot1, a1, b1, b0) break;                                      \
+    default: BATQ_STEP(S, slot1, slot0, a0, b2, b1) break;                                     \
+  }
+  if (NST > 0) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) BATQ_STEP6(s)
+  } else {
+    for (int64_t s = 0; s < nst; s += 6) {
+      BATQ_STEP(s, slot0, slot1, a1, b0, b2)
+      if (s + 1 < nst) BATQ_STEP(s + 1, slot1, slot0, a0, b1, b0)
+      if (s + 2 < nst) BATQ_STEP(s + 2, slot0, slot1, a1, b2, b1)
+      if (s + 3 < nst) BATQ_STEP(s + 3, slot1, slot0, a0, b0, b2)
+      if (s + 4 < nst) BATQ_STEP(s + 4, slot0, slot1, a1, b1, b0)
+      if (s + 5 < nst) BATQ_STEP(s + 5, slot1, slot0, a0, b2, b1)
+    }
+  }
+#undef BATQ_STEP6
+#undef BATQ_STEP
+#undef BATQ_CL
+
+  // Epilogue through LDS: one 32-row band per pass, 16-byte row chunks out.
+  float* epi = reinterpret_cast<float*>(epi_buf + wave * kEpiWave);
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+#pragma unroll
+    for (int k = 0; k < kNT; ++k)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rs = 8 * (r >> 2) + 4 * g + (r & 3);
+        epi[rs * kEpiStride + 32 * k + r32] = acc[i][k][r];
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * 4 * kNT / 64; ++it) {
+      const int id = it * 64 + lane;
+      const int rs = id / (4 * kNT);
+      const int cc = id % (4 * kNT);
+      const float* src = epi + rs * kEpiStride + 8 * cc;
+      const float4 lo = reinterpret_cast<const float4*>(src)[0];
+      const float4 hi = reinterpret_cast<const float4*>(src)[1];
+      const int64_t row = m0 + 32 * i + rs;
+      const int64_t col = n0 + 8 * cc;
+      if (row >= p.M || col >= p.N) continue;
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (p.out_f32) {
+        float* dst = reinterpret_cast<float*>(p.y) + row * p.N + col;
+        if (col + 8 <= p.N && p.vec_store) {
+          reinterpret_cast<float4*>(dst)[0] = lo;
+          reinterpret_cast<float4*>(dst)[1] = hi;
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = v[e];
+        }
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
+        uint32_t hb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hb[e] = f32_to_bf16_rne(v[e]);
+        if (col + 8 <= p.N && p.vec_store) {
+          *reinterpret_cast<uint4*>(dst) =
+              make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = (uint16_t)hb[e];
+        }
+      }
+    }
+  }
+}
+
+template <int NST>
+hipError_t launch_packed(const GemmArgs& args, hipStream_t stream) {
+  const int tiles_m = (int)((args.M + kBM - 1) / kBM);
+  const int tiles_n = (int)((args.N + kBN - 1) / kBN);
+  hipLaunchKernelGGL((mxfp4_gemm_packed_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_weight_pack(const uint8_t* wq, const uint8_t* ws, int64_t N, int64_t K, uint8_t* wp,
+                              hipStream_t stream) {
+  const int64_t groups = ((N + 31) / 32) * (K / 256);
+  hipLaunchKernelGGL(weight_pack_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, stream, wq, ws, N, K, wp);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream) {
+  switch (args.K / 256) {
+    case 1: return launch_packed<1>(args, stream);
+    case 2: return launch_packed<2>(args, stream);
+    case 4: return launch_packed<4>(args, stream);
+    case 8: return launch_packed<8>(args, stream);
+    case 16: return launch_packed<16>(args, stream);
+    case 48: return launch_packed<48>(args, stream);
+    default: return launch_packed<0>(args, stream);
+  }
+}
+
+}  // namespace batq
