@@ -160,8 +160,7 @@ batq_status batq_weight_pack(const uint8_t* Wq, const uint8_t* Ws, int64_t N, in
 
 /* Y[M][N] = deq(Xq,Xs) deq(W)^T with W given packed by batq_weight_pack; same
  * result as batq_mxfp4_gemm on the unpacked operands [en.papernotes.org, Key
- * Designs §1 and §4].  Xq 16-byte aligned, Xs 4-byte aligned, Wp 16-byte
- * aligned, Y 4-byte aligned.  M == 0 or N == 0 is a no-op.
+ * Designs §1 and §4].  Xq, Xs and Wp 16-byte aligned, Y 4-byte aligned.  M == 0 or N == 0 is a no-op.
  * Errors: NULL, SHAPE (K % 256 != 0), ALIGN, UNSUPPORTED (output type), HIP. */
 batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wp, int64_t M,
                                    int64_t N, int64_t K, void* Y, batq_out_dtype out, hipStream_t stream);

@@ -117,6 +117,7 @@ def test_packed_gemm_argument_checks(lib):
     assert f(FAKE, FAKE, 0, 4, 4, 256, FAKE, 0, None) == NULL
     assert f(FAKE + 8, FAKE, FAKE, 4, 4, 256, FAKE, 0, None) == ALIGN
     assert f(FAKE, FAKE + 2, FAKE, 4, 4, 256, FAKE, 0, None) == ALIGN
+    assert f(FAKE, FAKE + 4, FAKE, 4, 4, 256, FAKE, 0, None) == ALIGN
     assert f(FAKE, FAKE, FAKE + 4, 4, 4, 256, FAKE, 0, None) == ALIGN
     assert f(FAKE, FAKE, FAKE, 4, 4, 256, FAKE + 2, 0, None) == ALIGN
     assert f(FAKE, FAKE, FAKE, 0, 4, 256, FAKE, 0, None) == OK

@@ -193,7 +193,7 @@ batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const u
   if (M < 0 || N < 0 || K <= 0 || K % 256 != 0) return BATQ_ERR_SHAPE;
   if (out != BATQ_OUT_BF16 && out != BATQ_OUT_F32) return BATQ_ERR_UNSUPPORTED;
   if (Xq == nullptr || Xs == nullptr || Wp == nullptr || Y == nullptr) return BATQ_ERR_NULL;
-  if (!aligned(Xq, 16) || !aligned(Xs, 4) || !aligned(Wp, 16) || !aligned(Y, 4)) return BATQ_ERR_ALIGN;
+  if (!aligned(Xq, 16) || !aligned(Xs, 16) || !aligned(Wp, 16) || !aligned(Y, 4)) return BATQ_ERR_ALIGN;
   if (M == 0 || N == 0) return BATQ_OK;
   batq::GemmArgs args;
   args.xq = Xq;

@@ -18,9 +18,13 @@
 // Rows past N are zero codes with unit scales.
 //
 // Kernel: workgroup tile 128 (M) x 256 (N); wave w owns all 128 rows and
-// columns 64 w .. 64 w + 63 (4 x 2 MFMA tiles of 32 x 32).  Activations: a
-// three-slot direct-to-LDS ring (16 KB codes + 1 KB scales per stage).
-// Weights: three register sets (stages s, s+1, s+2 in flight).
+// columns 64 w .. 64 w + 63 (4 x 2 MFMA tiles of 32 x 32).  Activation codes
+// travel global -> registers -> a two-slot LDS ring (16 KB per stage, loaded
+// three stages ahead); weights go straight to registers (three sets, two
+// stages ahead).  Activation scales: a row's scales are 8 bytes per stage and
+// 128 rows apart, so when K / 256 is a multiple of 4 they are fetched four
+// stages at a time (one 16-byte load per thread instead of four 4-byte loads
+// that each touch 32 cache lines) into a two-group LDS ring.
 #include "common.h"
 
 namespace batq {
@@ -37,6 +41,7 @@ constexpr int kAScale = kBM * 8;                // 1 KB
 constexpr int kSlot = kAStage + kAScale;
 constexpr int kEpiStride = 32 * kNT + 8;        // floats
 constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes
+constexpr int kGroupM = 8;                      // row tiles per band of the tile order
 
 __device__ __forceinline__ i32x8 op(uint4 v) {
   i32x8 r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -134,7 +139,7 @@ __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_
     n##_1 = ld16(a_base1 + off_);                                                              \
     n##_2 = ld16(a_base2 + off_);                                                              \
     n##_3 = ld16(a_base3 + off_);                                                              \
-    n##_s = ld4(a_sbase + 8 * st_);                                                            \
+    if (!GS) n##_s = ld4(a_sbase + 8 * st_);                                                   \
   }
 #define BATQ_STORE_A(n, SLOT)                                                                  \
   {                                                                                            \
@@ -142,7 +147,18 @@ __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_
     a_dst(SLOT, tid + 256)[0] = n##_1;                                                         \
     a_dst(SLOT, tid + 512)[0] = n##_2;                                                         \
     a_dst(SLOT, tid + 768)[0] = n##_3;                                                         \
-    *reinterpret_cast<uint32_t*>((SLOT) + kAStage + 4 * tid) = n##_s;                          \
+    if (!GS) *reinterpret_cast<uint32_t*>((SLOT) + kAStage + 4 * tid) = n##_s;                 \
+  }
+// Grouped activation scales (GS): group G = stages 4G .. 4G+3.  Thread
+// (row tid / 2, half h = tid % 2) loads the 16 bytes of stages 4G + 2h and
+// 4G + 2h + 1 of its row; they are stored stage-major (1 KB per stage, 8 bytes
+// per row) so that the MMA's scale reads match the per-stage layout.
+#define BATQ_LOAD_AS(G) asg = ld16(a_gbase + 32 * opaque_stage(__builtin_amdgcn_readfirstlane((int)(G))));
+#define BATQ_STORE_AS(G)                                                                       \
+  {                                                                                            \
+    uint8_t* sg_ = (((G) & 1) ? sgrp1 : sgrp0) + 2048 * (tid & 1) + 8 * (tid >> 1);            \
+    *reinterpret_cast<uint2*>(sg_) = make_uint2(asg.x, asg.y);                                 \
+    *reinterpret_cast<uint2*>(sg_ + 1024) = make_uint2(asg.z, asg.w);                          \
   }
 
 // Stage-invariant per-thread source pointers (row clamped: rows past the edge
@@ -152,10 +168,10 @@ __device__ __forceinline__ const uint8_t* a_row_base(const GemmArgs& p, int64_t 
   gr = gr < p.M ? gr : p.M - 1;
   return p.xq + gr * (p.K >> 1) + 16 * (id & 7);
 }
-__device__ __forceinline__ const uint8_t* a_scale_base(const GemmArgs& p, int64_t m0, int tid) {
+__device__ __forceinline__ const uint8_t* a_scale_base(const GemmArgs& p, int64_t m0, int tid, int bytes) {
   int64_t gr = m0 + (tid >> 1);
   gr = gr < p.M ? gr : p.M - 1;
-  return p.xs + gr * (p.K >> 5) + 4 * (tid & 1);
+  return p.xs + gr * (p.K >> 5) + bytes * (tid & 1);
 }
 __device__ __forceinline__ uint4* a_dst(uint8_t* slot, int id) {
   const int row = id >> 3;
@@ -183,11 +199,11 @@ __device__ __forceinline__ void read_a(const uint8_t* As, int j, uint4 (&fa)[kMT
 
 // Stage from an LDS slot and a weight register set into the accumulators,
 // with the LDS reads of sub-step j+1 issued ahead of the MFMAs of sub-step j.
-#define BATQ_MMA_STAGE(SLOT, n)                                                                \
+#define BATQ_MMA_STAGE(SLOT, n, SCALES)                                                        \
   {                                                                                            \
     uint32_t sa_[kMT];                                                                         \
     _Pragma("unroll") for (int i = 0; i < kMT; ++i)                                            \
-      sa_[i] = ld4((SLOT) + kAStage + (32 * i + r32) * 8 + 4 * g);                             \
+      sa_[i] = ld4((SCALES) + (32 * i + r32) * 8 + 4 * g);                                     \
     uint4 fa0_[kMT], fa1_[kMT];                                                                \
     read_a(SLOT, 0, fa0_, r32, g);                                                             \
     read_a(SLOT, 1, fa1_, r32, g);                                                             \
@@ -207,10 +223,12 @@ __device__ __forceinline__ void read_a(const uint8_t* As, int j, uint4 (&fa)[kMT
 
 // NST > 0: stage count fixed at compile time, loop fully unrolled (exact
 // compiler wait counts).  NST == 0: runtime stage count.
-template <int NST>
+template <int NST, bool GS>
 __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlot];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[GS ? kAStage : kSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[GS ? kAStage : kSlot];
+  __shared__ __attribute__((aligned(1024))) uint8_t sgrp0[GS ? 4096 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sgrp1[GS ? 4096 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t epi_buf[4 * kEpiWave];
 
   const int tid = threadIdx.x;
@@ -220,9 +238,16 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
   const int g = lane >> 5;
   const int total = tiles_m * tiles_n;
   int t = blockIdx.x;
-  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);  // XCD-aware order
-  const int tm = t % tiles_m;
-  const int tn = t / tiles_m;
+  // XCD-aware order: consecutive workgroups go to the 8 XCDs in turn, so XCD x
+  // receives the contiguous range [x total / 8, (x + 1) total / 8) of t ...
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  // ... walked in bands of kGroupM row tiles, so that an XCD's concurrent
+  // workgroups share a small activation panel that stays in its L2.
+  const int gsz = kGroupM * tiles_n;
+  const int first_tm = (t / gsz) * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_tm);
+  const int tm = first_tm + (t % gsz) % gm;
+  const int tn = (t % gsz) / gm;
   const int64_t m0 = (int64_t)tm * kBM;
   const int64_t n0 = (int64_t)tn * kBN + 64 * wave;  // this wave's first column
   const int64_t n32_0 = n0 / 32;
@@ -252,11 +277,14 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
   const uint8_t* const a_base1 = a_row_base(p, m0, tid + 256);
   const uint8_t* const a_base2 = a_row_base(p, m0, tid + 512);
   const uint8_t* const a_base3 = a_row_base(p, m0, tid + 768);
-  const uint8_t* const a_sbase = a_scale_base(p, m0, tid);
+  const uint8_t* const a_sbase = a_scale_base(p, m0, tid, 4);   // per-stage scales
+  const uint8_t* const a_gbase = a_scale_base(p, m0, tid, 16);  // grouped scales
+  const int64_t ngrp = nst >> 2;
   const uint8_t* const b_base0 = b_src(p.wq, n32_g0, nst, 0) + 16 * lane;
   const uint8_t* const b_base1 = b_src(p.wq, n32_g1, nst, 0) + 16 * lane;
   BATQ_DECL_A(a0)
   BATQ_DECL_A(a1)
+  uint4 asg;
   BATQ_DECL_B(b0)
   BATQ_DECL_B(b1)
   BATQ_DECL_B(b2)
@@ -266,44 +294,64 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
     BATQ_LOAD_A(a1, BATQ_CL(1))
     BATQ_LOAD_B(b1, BATQ_CL(1))
   }
+  if (GS) BATQ_LOAD_AS(0)
   BATQ_STORE_A(a0, slot0)
+  if (GS) {
+    BATQ_STORE_AS(0)
+    if (NST == 0 || NST > 4) BATQ_LOAD_AS(ngrp > 1 ? 1 : 0)
+  }
   if (NST == 0 || NST > 2) BATQ_LOAD_A(a0, BATQ_CL(2))
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   block_barrier();
 
   // With a compile-time stage count the tail prefetches are simply omitted
   // (the conditions fold away); a runtime count keeps them, clamped.
-#define BATQ_STEP(S, CUR, NEXT, ANEXT, BCUR, BPF)                                               \
+// J: the step's phase modulo 12 (compile time); S: the step (may be runtime).
+#define BATQ_STEP(S, J, CUR, NEXT, ANEXT, BCUR, BPF)                                            \
   {                                                                                            \
     if (NST == 0 || (S) + 1 < NST) BATQ_STORE_A(ANEXT, NEXT)   /* act stage s+1 -> LDS */       \
+    if (GS && (J) % 4 == 0 && (NST == 0 || (S) + 4 < NST)) {   /* scale groups */              \
+      if (NST > 0 || (S) + 4 < nst) BATQ_STORE_AS(((S) >> 2) + 1)                              \
+      if (NST == 0 || (S) + 8 < NST)                                                           \
+        BATQ_LOAD_AS(((S) >> 2) + 2 < ngrp ? ((S) >> 2) + 2 : ngrp - 1)                        \
+    }                                                                                          \
     if (NST == 0 || (S) + 3 < NST) BATQ_LOAD_A(ANEXT, BATQ_CL((S) + 3)) /* act stage s+3 */     \
     if (NST == 0 || (S) + 2 < NST) BATQ_LOAD_B(BPF, BATQ_CL((S) + 2))   /* weight stage s+2 */  \
     sched_fence();                                                                             \
-    BATQ_MMA_STAGE(CUR, BCUR)                                                                  \
+    const uint8_t* scales_ = GS ? ((((S) >> 2) & 1) ? sgrp1 : sgrp0) + 1024 * ((J) % 4)        \
+                                : (CUR) + kAStage;                                             \
+    BATQ_MMA_STAGE(CUR, BCUR, scales_)                                                         \
     __builtin_amdgcn_s_waitcnt(0xC07F);          /* lgkmcnt(0): s+1 written, s read */         \
     block_barrier();                                                                           \
   }
   // Slots alternate with period 2 and weight sets with period 3.
 #define BATQ_STEP6(S)                                                                          \
   switch ((S) % 6) {                                                                           \
-    case 0: BATQ_STEP(S, slot0, slot1, a1, b0, b2) break;                                      \
-    case 1: BATQ_STEP(S, slot1, slot0, a0, b1, b0) break;                                      \
-    case 2: BATQ_STEP(S, slot0, slot1, a1, b2, b1) break;                                      \
-    case 3: BATQ_STEP(S, slot1, slot0, a0, b0, b2) break;                                      \
-    case 4: BATQ_STEP(S, slot0, slot1, a1, b1, b0) break;                                      \
-    default: BATQ_STEP(S, slot1, slot0, a0, b2, b1) break;                                     \
+    case 0: BATQ_STEP(S, S, slot0, slot1, a1, b0, b2) break;                                   \
+    case 1: BATQ_STEP(S, S, slot1, slot0, a0, b1, b0) break;                                   \
+    case 2: BATQ_STEP(S, S, slot0, slot1, a1, b2, b1) break;                                   \
+    case 3: BATQ_STEP(S, S, slot1, slot0, a0, b0, b2) break;                                   \
+    case 4: BATQ_STEP(S, S, slot0, slot1, a1, b1, b0) break;                                   \
+    default: BATQ_STEP(S, S, slot1, slot0, a0, b2, b1) break;                                  \
   }
   if (NST > 0) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) BATQ_STEP6(s)
   } else {
-    for (int64_t s = 0; s < nst; s += 6) {
-      BATQ_STEP(s, slot0, slot1, a1, b0, b2)
-      if (s + 1 < nst) BATQ_STEP(s + 1, slot1, slot0, a0, b1, b0)
-      if (s + 2 < nst) BATQ_STEP(s + 2, slot0, slot1, a1, b2, b1)
-      if (s + 3 < nst) BATQ_STEP(s + 3, slot1, slot0, a0, b0, b2)
-      if (s + 4 < nst) BATQ_STEP(s + 4, slot0, slot1, a1, b1, b0)
-      if (s + 5 < nst) BATQ_STEP(s + 5, slot1, slot0, a0, b2, b1)
+    // Period 12 = lcm(2 slots, 3 weight sets, 4 stages per scale group).
+    for (int64_t s = 0; s < nst; s += 12) {
+      BATQ_STEP(s, 0, slot0, slot1, a1, b0, b2)
+      if (s + 1 < nst) BATQ_STEP(s + 1, 1, slot1, slot0, a0, b1, b0)
+      if (s + 2 < nst) BATQ_STEP(s + 2, 2, slot0, slot1, a1, b2, b1)
+      if (s + 3 < nst) BATQ_STEP(s + 3, 3, slot1, slot0, a0, b0, b2)
+      if (s + 4 < nst) BATQ_STEP(s + 4, 4, slot0, slot1, a1, b1, b0)
+      if (s + 5 < nst) BATQ_STEP(s + 5, 5, slot1, slot0, a0, b2, b1)
+      if (s + 6 < nst) BATQ_STEP(s + 6, 6, slot0, slot1, a1, b0, b2)
+      if (s + 7 < nst) BATQ_STEP(s + 7, 7, slot1, slot0, a0, b1, b0)
+      if (s + 8 < nst) BATQ_STEP(s + 8, 8, slot0, slot1, a1, b2, b1)
+      if (s + 9 < nst) BATQ_STEP(s + 9, 9, slot1, slot0, a0, b0, b2)
+      if (s + 10 < nst) BATQ_STEP(s + 10, 10, slot0, slot1, a1, b1, b0)
+      if (s + 11 < nst) BATQ_STEP(s + 11, 11, slot1, slot0, a0, b2, b1)
     }
   }
 #undef BATQ_STEP6
@@ -359,11 +407,11 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
   }
 }
 
-template <int NST>
+template <int NST, bool GS>
 hipError_t launch_packed(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = (int)((args.M + kBM - 1) / kBM);
   const int tiles_n = (int)((args.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((mxfp4_gemm_packed_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+  hipLaunchKernelGGL((mxfp4_gemm_packed_kernel<NST, GS>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
                      tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -379,13 +427,14 @@ hipError_t launch_weight_pack(const uint8_t* wq, const uint8_t* ws, int64_t N, i
 
 hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream) {
   switch (args.K / 256) {
-    case 1: return launch_packed<1>(args, stream);
-    case 2: return launch_packed<2>(args, stream);
-    case 4: return launch_packed<4>(args, stream);
-    case 8: return launch_packed<8>(args, stream);
-    case 16: return launch_packed<16>(args, stream);
-    case 48: return launch_packed<48>(args, stream);
-    default: return launch_packed<0>(args, stream);
+    case 1: return launch_packed<1, false>(args, stream);
+    case 2: return launch_packed<2, false>(args, stream);
+    case 4: return launch_packed<4, true>(args, stream);
+    case 8: return launch_packed<8, true>(args, stream);
+    case 16: return launch_packed<16, true>(args, stream);
+    case 48: return launch_packed<48, true>(args, stream);
+    default:
+      return (args.K / 256) % 4 == 0 ? launch_packed<0, true>(args, stream) : launch_packed<0, false>(args, stream);
   }
 }
 
