@@ -177,19 +177,20 @@ def main():
             Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def act(i):
         s = sets[i % nsets]
-        if ev is not None:
-            ev[0].record()
         w.act_transform_quant(s["X"], A, B, rh, rl, out=(s["Xq"], s["Xs"]))
-        if ev is not None:
-            ev[1].record()
+
+    def gemm(i):
+        s = sets[i % nsets]
         if packed:
             w.mxfp4_gemm_packed(s["Xq"], s["Xs"], s["Wp"], out=s["Y"])
         else:
             w.mxfp4_gemm(s["Xq"], s["Xs"], s["Wq"], s["Ws"], out=s["Y"])
-        if ev is not None:
-            ev[2].record()
+
+    def step(i):
+        act(i)
+        gemm(i)
 
     for i in range(args.warmup):
         step(i)
@@ -203,14 +204,22 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per-kernel durations with HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t_act = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    # Per-kernel mean launch duration: `steps` back-to-back launches of one
+    # kernel over the same rotating buffers, between two HIP events recorded on
+    # the stream the kernels are launched on (torch's current stream).  One
+    # event pair per batch, so the events add no gap between launches.
+    def batch_seconds(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / args.steps
+
+    t_act = np.array([batch_seconds(act)])
+    t_gemm = np.array([batch_seconds(gemm)])
 
     flops = 2.0 * M * N * K
     act_bytes = M * K * 2 + M * K // 2 + M * K // 32  # algorithmic: read bf16, write codes + scales

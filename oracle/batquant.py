@@ -327,15 +327,20 @@ def bf16_values(bits: np.ndarray) -> np.ndarray:
 
 
 def act_transform_quant(X_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
-                        alpha: np.ndarray, beta: np.ndarray, exact: bool = False) -> Decisions:
+                        alpha: Optional[np.ndarray], beta: Optional[np.ndarray],
+                        exact: bool = False) -> Decisions:
     """Online activation path: y_b = x_b P_i, clip with sigmoid(alpha_i) * max and
-    sigmoid(beta_i) * min, MXFP4 quantise [en.papernotes.org, A Worked Example;
-    Key Designs §1-§3]."""
+    sigmoid(beta_i) * min (no clipping when the logits are None), MXFP4 quantise
+    [en.papernotes.org, A Worked Example; Key Designs §1-§3]."""
+    if (alpha is None) != (beta is None):
+        raise ValueError("alpha and beta must both be given or both be None")
     X = bf16_values(X_bits)
     P = block_matrices(A, B)
     Y = transform(X, P)
     S = transform_abs_sum(X, P)
-    return decisions(Y, S, clip_ratio(alpha), clip_ratio(beta), exact=exact)
+    rh = None if alpha is None else clip_ratio(alpha)
+    rl = None if beta is None else clip_ratio(beta)
+    return decisions(Y, S, rh, rl, exact=exact)
 
 
 def weight_prep(W_bits: np.ndarray, A: np.ndarray, B: np.ndarray,

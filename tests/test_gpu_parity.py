@@ -145,6 +145,32 @@ def test_act_zero_and_single_sign_blocks(w):
     assert same.all()
 
 
+def test_act_tiny_blocks_lowest_scale(w):
+    """Blocks whose maximum lies in [2^-126, 2^-124) take the lowest scale byte
+    (e = -127) yet still quantise to nonzero codes; some blocks of the same
+    rows are ordinary.  Identity factors keep every fp32 step exact."""
+    note("case: act tiny blocks at the lowest scale byte")
+    rng = np.random.default_rng(41)
+    M, K = 64, 256
+    x = rng.standard_normal((M, K))
+    # normal float32 magnitudes just above the smallest normal number
+    mags = np.array([1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5]) * 2.0 ** -126
+    tiny = rng.choice(mags, size=(M, 96)) * np.where(rng.random((M, 96)) < 0.5, -1.0, 1.0)
+    x[:, 32:128] = tiny
+    x[::3, 160:192] = tiny[::3, :32]  # some waves mix tiny and ordinary blocks
+    wl = gen.make_custom(M, K, 8, seed=41)
+    wl.X_bits = gen.f64_to_bf16_bits(x)
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (K // 32, 1, 1))
+    q, s = run_act(w, wl, A=A, B=B, clip=False)
+    dec = ob.act_transform_quant(wl.X_bits, A, B, None, None, exact=True)
+    codes = ob.unpack_codes(q)
+    assert np.all(dec.scales[:, 1:4] == 0) and np.any(dec.codes[:, 32:128] & 7)
+    assert np.array_equal(s, dec.scales)
+    same = (codes == dec.codes) | (dec.zero_sign_free & ((codes & 7) == 0) & ((dec.codes & 7) == 0))
+    assert same.all(), np.argwhere(~same)[:5].tolist()
+
+
 def test_act_locality_and_determinism(w):
     note("case: act locality (re-randomised block) and determinism")
     wl = gen.make_custom(128, 1024, 8, seed=41)

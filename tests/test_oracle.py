@@ -471,3 +471,27 @@ def test_exempt_window_stays_narrow(cfg):
     n = d.codes.size
     assert d.n_exempt / n < 5e-5, (d.n_exempt, n)
     assert not np.any(d.zero_sign_free)
+
+
+def test_no_clip_is_the_plain_quantiser_and_tiny_blocks_use_the_lowest_scale():
+    """No logits means no clipping: with identity factors the result is the
+    plain OCP MX quantiser of x.  Blocks whose maximum lies just above the
+    smallest normal float take scale byte 0 (e = -127) and nonzero codes,
+    which the closed form fixes: x / 2^-127 for x = k 2^-126 is 2k."""
+    K = 64
+    x = np.zeros((2, K))
+    x[:, :32] = np.array([1.0, 1.5, 2.0, 3.5] * 8) * 2.0 ** -126
+    x[1, :32] *= -1
+    x[:, 32:] = 0.7
+    bits = gen.f64_to_bf16_bits(x)
+    A = np.eye(8, dtype=np.float32)
+    B = np.tile(np.eye(4, dtype=np.float32), (K // 32, 1, 1))
+    dec = ob.act_transform_quant(bits, A, B, None, None, exact=True)
+    assert dec.scales[:, 0].tolist() == [0, 0]
+    # 2k for k = 1, 1.5, 2, 3.5 -> 2, 3, 4, 7 (nearest E2M1: 2, 3, 4, 6) -> codes 4, 5, 6, 7
+    assert dec.codes[0, :4].tolist() == [4, 5, 6, 7]
+    assert dec.codes[1, :4].tolist() == [12, 13, 14, 15]
+    # 0.7: e = floor(log2 0.7) - 2 = -3, 0.7 * 8 = 5.6 -> 6 (code 7)
+    assert dec.scales[0, 1] == 124 and dec.codes[0, 32] == 7
+    with pytest.raises(ValueError):
+        ob.act_transform_quant(bits, A, B, None, np.zeros(2, np.float32))

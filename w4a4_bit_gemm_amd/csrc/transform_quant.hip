@@ -30,7 +30,12 @@ namespace batq {
 
 namespace {
 
-constexpr int kWavesPerWG = 8;  // one 32-channel block per wave; 8 blocks = 128 code bytes per row
+constexpr int kBlocksPerWG = 8;  // one 32-channel block per compute wave; 8 blocks = 128 code bytes per row
+constexpr int kLoaderWave = kBlocksPerWG - 1;  // also issues the global -> LDS tile loads
+constexpr int kStorerWave = kBlocksPerWG - 2;  // also writes the staged codes and scales
+constexpr int kThreads = 64 * kBlocksPerWG;
+constexpr int kTT = 32;                        // tokens per tile (one MFMA group)
+constexpr int kRing = 4;                       // LDS tile slots; kRing - 1 tiles in flight
 
 // Exact product pa * pb split into three bf16 parts, hi + mid + lo, whose sum
 // differs from the product by at most ~2^-27 of it.
@@ -54,61 +59,83 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Tile of one workgroup: TT tokens x 8 consecutive blocks (256 channels).
-//  1. The bf16 tile (TT x 512 bytes) moves global -> LDS with 16-byte
-//     direct-to-LDS loads, one instruction = two whole 512-byte row segments.
-//     Row r keeps its 16-byte chunk c at position c ^ (r & 15), so the MFMA
-//     operand reads below (16 consecutive rows, same chunk) hit 16 different
-//     bank groups.
-//  2. While those loads fly, each wave (one block) builds its P_i split.
-//  3. Per 32-token group: MFMA transform, clip, scale, E2M1 codes; codes and
-//     scale bytes go to LDS staging buffers.
-//  4. Codes leave in 16-byte row-contiguous chunks (whole 128-byte lines per
-//     row of the tile); scale bytes in 8-byte row pieces.
-template <int TT>
-struct TQTile {
+// Two 16-byte LDS reads that complete inside the same asm block.  Written
+// as asm because the compiler cannot tell these reads from the slots that
+// direct-to-LDS loads are still filling, and would otherwise wait for every
+// load in flight; the loader's exact wait and the barrier before the reads
+// already order them after the tile's own loads.
+__device__ __forceinline__ void lds_read2_b128(const uint8_t* p0, const uint8_t* p1, uint4& v0, uint4& v1) {
+  const uint32_t a0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p0;
+  const uint32_t a1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p1;
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Persistent workgroup: one column of 8 blocks (256 channels) and the token
+// tiles ty = blockIdx.y, blockIdx.y + gridDim.y, ... (32 tokens each), with
+// two workgroups resident per CU.  Every wave w computes block blk0 + w: it
+// builds its P_i split once, then per tile runs the MFMA transform, clip,
+// scale and E2M1 codes into LDS staging buffers.  Two waves have a second
+// role, chosen so that no wave's memory-counter waits ever cover another
+// kind of traffic:
+//   loader (wave 7)   keeps kRing - 1 tiles in flight: 16-byte direct-to-LDS
+//                     loads, one instruction = two whole 512-byte row segments;
+//                     row r keeps its 16-byte chunk c at position c ^ (r & 15),
+//                     so the MFMA operand reads (16 consecutive rows, same
+//                     chunk) hit 16 different bank groups.  It issues no
+//                     stores, so its wait for a tile is an exact count;
+//   storer (wave 6)   writes the staged codes as 16-byte row-contiguous chunks
+//                     (whole 128-byte lines per row) and the scales as 8-byte
+//                     row pieces.  It never waits for its stores.
+// Per tile i, two workgroup barriers: A_i (tile i is in LDS; staging is free)
+// and B_i (tile i's codes and scales are staged).
+struct TQSmem {
   static constexpr int kXRow = 512;        // bytes per staged bf16 row (256 channels)
-  static constexpr int kX = TT * kXRow;
+  static constexpr int kX = kTT * kXRow;   // one tile slot
   static constexpr int kQRow = 144;        // 128 code bytes + 16 pad: conflict-free 8-byte writes
-  static constexpr int kQ = TT * kQRow;
-  static constexpr int kS = TT * 8;
 };
 
-template <int TT>
-__global__ __launch_bounds__(512) void transform_quant_kernel(TransformQuantArgs p) {
-  using T = TQTile<TT>;
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[T::kX];
-  __shared__ __attribute__((aligned(16))) uint8_t qs[T::kQ];
-  __shared__ __attribute__((aligned(16))) uint8_t ss[T::kS];
+// PER_ROW: one ratio pair per (row, block), read per tile (the weight side);
+// otherwise one pair per block, read once (activations), which keeps every
+// memory wait out of the activations' tile loop.
+template <bool PER_ROW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
+    TransformQuantArgs p) {
+  using T = TQSmem;
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[kRing * T::kX];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kTT * T::kQRow];
+  __shared__ __attribute__((aligned(16))) uint8_t ss[kTT * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t nb = p.K >> 5;
-  const int64_t blk0 = (int64_t)blockIdx.x * kWavesPerWG;
+  const int64_t blk0 = (int64_t)blockIdx.x * kBlocksPerWG;
+  const int64_t tiles = (p.rows + kTT - 1) / kTT;
+  const int64_t ty0 = blockIdx.y;
+  const int64_t tstep = gridDim.y;
+  const int64_t ntile = ty0 < tiles ? (tiles - ty0 + tstep - 1) / tstep : 0;  // uniform per workgroup
+  const int64_t nblk = (nb - blk0) < kBlocksPerWG ? (nb - blk0) : kBlocksPerWG;  // valid blocks here
+
+  // ---------------------------------------------------------- compute waves
   const int64_t blk = blk0 + wave;
-  const bool blk_ok = blk < nb;  // waves past the last block still load and sync
-  const int64_t tok0 = (int64_t)blockIdx.y * TT;
-
-  // 1. global -> LDS: TT / 2 instructions of 1 KB, TT / 16 per wave
-#pragma unroll
-  for (int i = 0; i < TT / 16; ++i) {
-    const int q = wave + kWavesPerWG * i;
-    const int row = 2 * q + (lane >> 5);
-    const int pc = lane & 31;              // position in the staged row
-    const int c = pc ^ (row & 15);         // logical 16-byte chunk stored there
-    int64_t gr = tok0 + row;
-    gr = gr < p.rows ? gr : p.rows - 1;    // rows past the end re-read the last row
-    int64_t col = blk0 * 32 + 8 * c;       // first channel of the chunk
-    col = col < p.K ? col : 0;             // chunks past K read a valid column, unused
-    __builtin_amdgcn_global_load_lds(p.x + gr * p.ldx + col, (lds_void*)(xs + q * 1024), 16, 0, 0);
-  }
-
+  const bool blk_ok = blk < nb;  // waves past the last block only keep the barriers
   const int j = lane & 31;  // output channel (A-operand row) / token slot (B column)
   const int h = lane >> 5;  // which 8-channel half of each 16-channel k step
 
-  // 2. P_i^T as MFMA A operand: lane holds P_i[16 ks + 8 h + t][j], t = 0..7,
-  //    as an exact three-way bf16 split.
+  // P_i^T as MFMA A operand: lane holds P_i[16 ks + 8 h + t][j], t = 0..7, as
+  // an exact three-way bf16 split.
   const int la = p.a_log2;
   const int a = 1 << la;
   const int amask = a - 1;
@@ -131,17 +158,80 @@ __global__ __launch_bounds__(512) void transform_quant_kernel(TransformQuantArgs
       plo[ks] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
-  block_barrier();                      // ... and every other wave's
+  // Ratios shared by every token (activations) are read once here.
+  const bool clip = p.r_hi != nullptr;
+  const bool per_row = PER_ROW && clip;
+  float rh_blk = 1.0f, rl_blk = 1.0f;
+  if (clip && !per_row && blk_ok) {
+    rh_blk = p.r_hi[blk];
+    rl_blk = p.r_lo[blk];
+  }
 
-  // 3. per 32-token group
-  if (blk_ok) {
+  // Loader: tile i (< ntile) -> its slot; one tile is kTT / 2 load instructions,
+  // instruction q covering rows 2q and 2q + 1.  Lane l fetches row
+  // 2q + l / 32, logical 16-byte chunk c = (l % 32) ^ (row % 16) (chunks past K
+  // read a valid column, unused).  The swizzle repeats every 8 instructions, so
+  // the lane's offset within the tile is precomputed for q = 0..7; a full tile
+  // then costs one 64-bit add per instruction.
+  const bool loader = wave == kLoaderWave;
+  // Loader addressing: a buffer descriptor based at the tile's first row whose
+  // size ends at the last row of X (the hardware range check turns rows past
+  // the end into zeros, which are never stored), plus per-lane byte offsets
+  // within the tile.  Instruction q covers rows 2q and 2q + 1: lane l fetches
+  // row 2q + l / 32, logical 16-byte chunk c = (l % 32) ^ (row % 16) (chunks
+  // past K read a valid column, unused).  The swizzle repeats every 8
+  // instructions, so 8 offsets serve all 16; rows 16..31 add a scalar offset.
+  const uint32_t ld2 = (uint32_t)(p.ldx * 2);  // row stride in bytes
+  uint32_t voff[8];
 #pragma unroll
-    for (int gi = 0; gi < TT / 32; ++gi) {
-      const int row = 32 * gi + j;
-      const uint8_t* xr = xs + row * T::kXRow;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(xr + 16 * ((4 * wave + h) ^ (row & 15)));
-      const uint4 x1 = *reinterpret_cast<const uint4*>(xr + 16 * ((4 * wave + 2 + h) ^ (row & 15)));
+  for (int q = 0; q < 8; ++q) {
+    const int row = 2 * q + (lane >> 5);
+    const int c = (lane & 31) ^ (row & 15);
+    const int64_t col = blk0 * 32 + 8 * c;
+    voff[q] = (uint32_t)row * ld2 + (col < p.K ? (uint32_t)(col * 2) : 0u);
+  }
+  const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
+  auto load_tile = [&](int64_t i, int slot) {
+    const int64_t tok0 = (ty0 + i * tstep) * kTT;
+    const int64_t left = (p.rows - tok0) * (int64_t)ld2;  // bytes from the tile's first row to the end of X
+    const int nrec = left < 0x7FFFFFFF ? (int)left : 0x7FFFFFFF;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(xb + tok0 * (int64_t)ld2), (short)0, nrec, 0x00020000);
+    uint8_t* dst = xs + slot * T::kX;
+#pragma unroll
+    for (int q = 0; q < kTT / 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + q * 1024), 16, (int)voff[q & 7],
+                                               (int)((q >> 3) * 16 * ld2), 0, 0);
+  };
+  if (loader) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the factor loads above are not counted below
+    for (int i = 0; i < kRing - 1; ++i)
+      if (i < ntile) load_tile(i, i);
+  }
+  static_assert(kRing == 4, "the loader's wait distinguishes 0, 1 or 2 younger tiles");
+  const int64_t qld = p.K >> 1;
+
+  for (int64_t i = 0; i < ntile; ++i) {
+    if (loader) {
+      // tile i has landed once at most the younger tiles' loads are pending
+      const int64_t younger = ntile - 1 - i;
+      if (younger >= 2) {
+        wait_vmcnt<2 * (kTT / 2)>();
+      } else if (younger == 1) {
+        wait_vmcnt<kTT / 2>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    block_barrier();  // A_i: tile i is in its slot; the previous staging has been read
+    if (loader && i + kRing - 1 < ntile) load_tile(i + kRing - 1, (int)((i + kRing - 1) % kRing));
+    const int64_t tok0 = (ty0 + i * tstep) * kTT;
+    if (blk_ok) {
+      const uint8_t* xt = xs + (int)(i % kRing) * T::kX;
+      const int row = j;
+      const uint8_t* xr = xt + row * T::kXRow;
+      uint4 x0, x1;
+      lds_read2_b128(xr + 16 * ((4 * wave + h) ^ (row & 15)), xr + 16 * ((4 * wave + 2 + h) ^ (row & 15)), x0, x1);
       f32x16 acc = {};
       const bf16x8 bx0 = as_bf16x8(x0), bx1 = as_bf16x8(x1);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(plo[0]), bx0, acc, 0, 0, 0);
@@ -158,13 +248,18 @@ __global__ __launch_bounds__(512) void transform_quant_kernel(TransformQuantArgs
         mx = fmaxf(mx, acc[r]);
         mn = fminf(mn, acc[r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mn = fminf(mn, __shfl_xor(mn, 32));
+      {
+        // lanes l and l ^ 32 hold the two halves of a token's 32 channels
+        const auto smx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        const auto smn = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+        mx = fmaxf(__uint_as_float(smx[0]), __uint_as_float(smx[1]));
+        mn = fminf(__uint_as_float(smn[0]), __uint_as_float(smn[1]));
+      }
 
-      int64_t tok = tok0 + row;
-      tok = tok < p.rows ? tok : p.rows - 1;
-      float rh = 1.0f, rl = 1.0f;
-      if (p.r_hi != nullptr) {
+      float rh = rh_blk, rl = rl_blk;
+      if (per_row) {
+        int64_t tok = tok0 + row;
+        tok = tok < p.rows ? tok : p.rows - 1;
         const int64_t ri = tok * p.r_ld + blk;
         rh = p.r_hi[ri];
         rl = p.r_lo[ri];
@@ -176,27 +271,38 @@ __global__ __launch_bounds__(512) void transform_quant_kernel(TransformQuantArgs
       const float amax = fmaxf(fabsf(zmax), fabsf(zmin));
       // scale byte = e + 127 = max(biased exponent of amax - 2, 0)
       const int sbyte = max((int)(__float_as_uint(amax) >> 23) - 2, 0);
-      const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-e, exact
 
+      // The converter divides by its scale operand, so 2^e goes in directly
+      // (z / 2^e is exact).  2^-127 (scale byte 0, a block below 2^-125) is
+      // not a normal float: such waves take the explicit multiply by 2^-e.
       uint32_t wA = 0, wB = 0;
-#define BATQ_CVT(word, r, sel)                                                        \
+#define BATQ_CVT(word, r, sel, M, S)                                                  \
   word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(                                    \
-      word, __builtin_amdgcn_fmed3f(acc[r], l, u) * inv,                              \
-      __builtin_amdgcn_fmed3f(acc[r + 1], l, u) * inv, 1.0f, sel)
-      BATQ_CVT(wA, 0, 0);
-      BATQ_CVT(wA, 2, 1);
-      BATQ_CVT(wA, 4, 2);
-      BATQ_CVT(wA, 6, 3);
-      BATQ_CVT(wB, 8, 0);
-      BATQ_CVT(wB, 10, 1);
-      BATQ_CVT(wB, 12, 2);
-      BATQ_CVT(wB, 14, 3);
+      word, __builtin_amdgcn_fmed3f(acc[r], l, u) M, __builtin_amdgcn_fmed3f(acc[r + 1], l, u) M, S, sel)
+#define BATQ_CVT_ALL(M, S)                                                            \
+  BATQ_CVT(wA, 0, 0, M, S);                                                           \
+  BATQ_CVT(wA, 2, 1, M, S);                                                           \
+  BATQ_CVT(wA, 4, 2, M, S);                                                           \
+  BATQ_CVT(wA, 6, 3, M, S);                                                           \
+  BATQ_CVT(wB, 8, 0, M, S);                                                           \
+  BATQ_CVT(wB, 10, 1, M, S);                                                          \
+  BATQ_CVT(wB, 12, 2, M, S);                                                          \
+  BATQ_CVT(wB, 14, 3, M, S);
+      if (__builtin_amdgcn_ballot_w64(sbyte == 0) == 0) {
+        const float scale = __uint_as_float((uint32_t)sbyte << 23);  // 2^e
+        BATQ_CVT_ALL(, scale)
+      } else {
+        const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-e, exact
+        BATQ_CVT_ALL(*inv, 1.0f)
+      }
+#undef BATQ_CVT_ALL
 #undef BATQ_CVT
       // Lane half h holds code bytes {4q + 2h, 4q + 2h + 1}, q = 0..3, with
       // q = 0,1 in wA and q = 2,3 in wB.  Swap so that half 0 holds bytes 0..7
       // and half 1 bytes 8..15 of the token's 16-byte code segment.
       const uint32_t send = h ? wA : wB;
-      const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+      const auto sw = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+      const uint32_t recv = h ? sw[0] : sw[1];  // the partner lane's word
       const uint32_t keep = h ? wB : wA;
       const uint32_t first = h ? recv : keep;
       const uint32_t second = h ? keep : recv;
@@ -205,34 +311,30 @@ __global__ __launch_bounds__(512) void transform_quant_kernel(TransformQuantArgs
       *reinterpret_cast<uint2*>(qs + row * T::kQRow + 16 * wave + 8 * h) = make_uint2(out_lo, out_hi);
       if (h == 0) ss[row * 8 + wave] = (uint8_t)sbyte;
     }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged codes and scales written
-  block_barrier();
-
-  // 4. codes: TT rows x up to 128 bytes in 16-byte chunks
-  const int64_t qld = p.K >> 1;
-  const int64_t nblk = (nb - blk0) < kWavesPerWG ? (nb - blk0) : kWavesPerWG;  // valid blocks in tile
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    block_barrier();                      // B_i
+    if (wave == kStorerWave) {
 #pragma unroll
-  for (int i = 0; i < (TT * 8 + 511) / 512; ++i) {
-    const int id = tid + 512 * i;
-    if (id >= TT * 8) break;
-    const int row = id >> 3;
-    const int c = id & 7;
-    const int64_t tok = tok0 + row;
-    if (tok < p.rows && c < nblk)
-      *reinterpret_cast<uint4*>(p.q + tok * qld + blk0 * 16 + 16 * c) =
-          *reinterpret_cast<const uint4*>(qs + row * T::kQRow + 16 * c);
-  }
-  //    scales: one thread per row
-  if (tid < TT) {
-    const int64_t tok = tok0 + tid;
-    if (tok < p.rows) {
-      uint8_t* dst = p.s + tok * nb + blk0;
-      const uint8_t* src = ss + tid * 8;
-      if (nblk == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
-      } else {
-        for (int c = 0; c < nblk; ++c) dst[c] = src[c];
+      for (int k = 0; k < kTT * 8 / 64; ++k) {
+        const int id = lane + 64 * k;
+        const int row = id >> 3;
+        const int c = id & 7;
+        const int64_t tok = tok0 + row;
+        if (tok < p.rows && c < nblk)
+          *reinterpret_cast<uint4*>(p.q + tok * qld + blk0 * 16 + 16 * c) =
+              *reinterpret_cast<const uint4*>(qs + row * T::kQRow + 16 * c);
+      }
+      if (lane < kTT) {
+        const int64_t tok = tok0 + lane;
+        if (tok < p.rows) {
+          uint8_t* dst = p.s + tok * nb + blk0;
+          const uint8_t* src = ss + lane * 8;
+          if (nblk == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+          } else {
+            for (int c = 0; c < nblk; ++c) dst[c] = src[c];
+          }
+        }
       }
     }
   }
@@ -242,19 +344,20 @@ __global__ __launch_bounds__(512) void transform_quant_kernel(TransformQuantArgs
 
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream) {
   const int64_t nb = args.K >> 5;
-  const unsigned gx = (unsigned)((nb + kWavesPerWG - 1) / kWavesPerWG);
-  // Tokens per workgroup: 64 (three resident workgroups per CU, 42 KB of LDS
-  // each), 128 for layers too small to give every CU two workgroups of 64,
-  // 32 for a handful of tokens.
-  int tt = 64;
-  if ((int64_t)gx * ((args.rows + 63) / 64) < 512) tt = 128;
-  if (args.rows <= 32) tt = 32;
-  dim3 grid(gx, (unsigned)((args.rows + tt - 1) / tt));
-  switch (tt) {
-    case 128: hipLaunchKernelGGL(transform_quant_kernel<128>, grid, dim3(512), 0, stream, args); break;
-    case 64: hipLaunchKernelGGL(transform_quant_kernel<64>, grid, dim3(512), 0, stream, args); break;
-    default: hipLaunchKernelGGL(transform_quant_kernel<32>, grid, dim3(512), 0, stream, args); break;
-  }
+  const int64_t gx = (nb + kBlocksPerWG - 1) / kBlocksPerWG;
+  const int64_t tiles = (args.rows + kTT - 1) / kTT;
+  // Two workgroups fit per CU (70 KB of LDS each); size the grid to about one
+  // resident round and let each workgroup walk its column's tiles.
+  const int64_t target = 512;
+  int64_t gy = target / gx;
+  if (gy < 1) gy = 1;
+  if (gy > tiles) gy = tiles;
+  if (gy > 65535) gy = 65535;
+  dim3 grid((unsigned)gx, (unsigned)gy);
+  if (args.r_hi != nullptr && args.r_ld != 0)
+    hipLaunchKernelGGL(transform_quant_kernel<true>, grid, dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL(transform_quant_kernel<false>, grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
