@@ -57,9 +57,10 @@ def kernel_source_digest(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_file: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
-    they were taken on the current kernel source."""
+def load_traffic(kernel_file: str, kernel: str, workload: str):
+    """HBM bytes per launch (fetched + written, calibrated) from the committed
+    rocprofv3 counter summary, only if it was taken on the current kernel
+    source, for this kernel instance and workload."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -67,8 +68,10 @@ def load_traffic(kernel_file: str):
     with open(path) as f:
         for ln in f:
             parts = ln.split()
-            if len(parts) >= 4 and not ln.startswith("#") and parts[0] == kernel_file and parts[1] == want:
-                return float(parts[2]) + float(parts[3])  # fetched + written bytes, calibrated
+            if ln.startswith("#") or len(parts) != 6:
+                continue
+            if parts[0] == kernel_file and parts[1] == kernel and parts[2] == want and parts[5] == workload:
+                return float(parts[3]) + float(parts[4])
     return None
 
 
@@ -239,11 +242,15 @@ def main():
     dominant_is_gemm = t_gemm.mean() >= t_act.mean()
     roof = dict(gemm_roof if dominant_is_gemm else act_roof)
     gemm_src = "mxfp4_gemm_packed.hip" if packed else "mxfp4_gemm.hip"
-    gemm_kernel = "mxfp4_gemm_packed_kernel" if packed else "mxfp4_gemm_dma_kernel"
-    traffic = load_traffic(gemm_src if dominant_is_gemm else "transform_quant.hip")
-    roof["traffic"] = traffic
-    roof["kernel"] = gemm_kernel if dominant_is_gemm else "transform_quant_kernel"
-    act_roof["traffic"] = load_traffic("transform_quant.hip")
+    nst = K // 256
+    gs = "true" if nst % 4 == 0 else "false"
+    gemm_kernel = (f"mxfp4_gemm_packed_kernel<{nst if nst in (1, 2, 4, 8, 16, 48) else 0},{gs}>" if packed
+                   else "mxfp4_gemm_dma_kernel")
+    act_kernel = "transform_quant_kernel<false>"
+    act_roof["traffic"] = load_traffic("transform_quant.hip", act_kernel, wl.name)
+    gemm_roof["traffic"] = load_traffic(gemm_src, gemm_kernel, wl.name)
+    roof["traffic"] = gemm_roof["traffic"] if dominant_is_gemm else act_roof["traffic"]
+    roof["kernel"] = gemm_kernel if dominant_is_gemm else act_kernel
 
     out = {
         "metric": METRIC,
@@ -271,7 +278,7 @@ def main():
                                 "roofline": act_roof},
             "mxfp4_gemm": {"kernel": gemm_kernel, "us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
                            "frac_mfma": gemm_tflops / MXFP4_PEAK_TFLOPS, "flops": flops,
-                           "operand_output_bytes": gemm_bytes},
+                           "operand_output_bytes": gemm_bytes, "roofline": gemm_roof},
         },
         "cpu_baseline": None,
     }
