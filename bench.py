@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--a", type=int, default=8, help="shared factor size (config 5 sweep)")
+    ap.add_argument("--factors", choices=["gpk", "hadamard"], default="gpk",
+                    help="transform factors: seeded near-identity GPK, or the block-Hadamard rotation (BRQ)")
+    ap.add_argument("--no-clip", action="store_true", help="no block-wise clipping (activations and weights)")
     ap.add_argument("--gemm", choices=["packed", "unpacked"], default="packed",
                     help="weight operand layout of the GEMM (packed: lane-ordered, prepared offline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,11 +159,15 @@ def main():
     def f32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
+    if args.factors == "hadamard":
+        wl.A, wl.B = gen.hadamard_factors(K, wl.a)
+    if args.no_clip:
+        wl.alpha = wl.beta = wl.walpha = wl.wbeta = None
     X0 = bf16(wl.X_bits)
     A = f32(wl.A)
     B = f32(wl.B)
-    rh = f32(w.clip_ratios(wl.alpha))
-    rl = f32(w.clip_ratios(wl.beta))
+    rh = None if args.no_clip else f32(w.clip_ratios(wl.alpha))
+    rl = None if args.no_clip else f32(w.clip_ratios(wl.beta))
     Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)  # offline
     packed = args.gemm == "packed"
     Wp0 = w.weight_pack(Wq0, Ws0) if packed else None  # offline
@@ -267,9 +274,12 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), "
-                        f"W {N}x{K} bf16 N(0,0.02) prepared offline ({args.gemm} MXFP4); GPK a={wl.a} b={wl.b}; "
+                        f"W {N}x{K} bf16 N(0,0.02) prepared offline ({args.gemm} MXFP4); "
+                        f"{'block-Hadamard (BRQ) factors' if args.factors == 'hadamard' else 'GPK'} a={wl.a} b={wl.b}"
+                        f"{', no clipping' if args.no_clip else ''}; "
                         f"step = act transform+clip+MXFP4 quant + MXFP4 GEMM (bf16 out)",
             "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets, "gemm": args.gemm,
+            "factors": args.factors, "clip": not args.no_clip,
         },
         "roofline": roof,
         "kernels": {

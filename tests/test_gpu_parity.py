@@ -446,3 +446,47 @@ def test_packed_end_to_end_full_config(w, cfg):
     rel = np.abs(y - ref).max() / np.abs(ref).max()
     note(f"  max rel err {rel:.3e}")
     assert rel <= 1e-2  # bf16 output rounding on top of the fp32 bound
+
+
+
+# ------------------------------------------- block-Hadamard (BRQ) special case
+
+
+@pytest.mark.parametrize("cfg,clip", [(1, False), (2, False), (2, True), (3, False)])
+def test_act_block_hadamard(w, cfg, clip):
+    """The block rotation of the BRQ article is the GPK transform with
+    A = H_8 / sqrt(8), B_i = H_4 / 2 (P_i = H_32 / sqrt(32)); same kernel, same
+    parity rules, with and without the block-wise clipping."""
+    note(f"case: act block-Hadamard config {cfg} clip={clip}")
+    wl = gen.make_workload(cfg, with_weights=False)
+    A, B = gen.hadamard_factors(wl.K)
+    q, s = run_act(w, wl, A=A, B=B, clip=clip)
+    rows = np.arange(wl.M) if wl.M <= 1024 else _sample_rows(wl.M, 1024, 300 + cfg)
+    dec = ob.act_transform_quant(wl.X_bits[rows], A, B, wl.alpha if clip else None, wl.beta if clip else None)
+    st = parity.compare_quant(q[rows], s[rows], dec, label=f"hadamard config {cfg} clip={clip}")
+    note(f"  {st}")
+
+
+def test_block_hadamard_end_to_end(w):
+    """Block-Hadamard chain X, W -> Y: the weight side uses P^-T = P (orthogonal,
+    symmetric); sampled outputs against the oracle chain, and the packed GEMM
+    equals the unpacked one."""
+    note("case: block-Hadamard end to end (config 2)")
+    wl = gen.make_workload(2)
+    A, B = gen.hadamard_factors(wl.K)
+    xq, xs = w.act_transform_quant(dev_bf16(wl.X_bits), dev_f32(A), dev_f32(B), None, None)
+    wq, ws = w.prepare_weight(dev_bf16(wl.W_bits), A, B, None, None)
+    wp = w.weight_pack(wq, ws)
+    Yp = w.mxfp4_gemm_packed(xq, xs, wp, out_dtype=torch.float32)
+    Yu = w.mxfp4_gemm(xq, xs, wq, ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(Yp, Yu)
+    rows = _sample_rows(wl.M, 16, 901)
+    cols = _sample_rows(wl.N, 16, 902)
+    x = ob.act_transform_quant(wl.X_bits[rows], A, B, None, None)
+    wt = ob.weight_prep(wl.W_bits[cols], A, B, None, None)
+    ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
+    y = Yp[rows][:, cols].cpu().numpy().astype(np.float64)
+    rel = np.abs(y - ref).max() / np.abs(ref).max()
+    note(f"  max rel err {rel:.3e}")
+    assert rel <= 1e-3

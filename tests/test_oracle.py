@@ -495,3 +495,13 @@ def test_no_clip_is_the_plain_quantiser_and_tiny_blocks_use_the_lowest_scale():
     assert dec.scales[0, 1] == 124 and dec.codes[0, 32] == 7
     with pytest.raises(ValueError):
         ob.act_transform_quant(bits, A, B, None, np.zeros(2, np.float32))
+
+
+def test_hadamard_factor_recipe_is_the_block_rotation():
+    """The workload recipe's block-Hadamard factors give P_i = H_32 / sqrt(32)
+    (checked against scipy's Sylvester construction) for every (a, b)."""
+    for a in gen.SWEEP_A:
+        A, B = gen.hadamard_factors(64, a)
+        P = ob.block_matrices(A, B)
+        assert P.shape == (2, 32, 32)
+        assert np.allclose(P[1], scipy.linalg.hadamard(32) / math.sqrt(32), atol=1e-6)

@@ -128,6 +128,24 @@ def make_factors(cfg: int, K: int, a: int, sweep: bool = False):
     return A.astype(np.float32), B.astype(np.float32)
 
 
+def _sylvester(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_factors(K: int, a: int = 8):
+    """Block-Hadamard factors, float32: A = H_a / sqrt(a) and every B_i =
+    H_b / sqrt(b) (b = 32 / a), so that P_i = B_i (x) A = H_32 / sqrt(32)
+    (Sylvester ordering), the block rotation of the BRQ article (10100.com)."""
+    b = 32 // a
+    A = (_sylvester(a) / np.sqrt(a)).astype(np.float32)
+    B = np.tile((_sylvester(b) / np.sqrt(b)).astype(np.float32), (K // 32, 1, 1))
+    return A, B
+
+
 def make_workload(cfg: int, a: int = 8, M: Optional[int] = None, with_weights: bool = True) -> Workload:
     """Build config ``cfg`` (1..5).  ``M`` overrides the token count (rows are
     drawn for the full config and the first M kept, so a smaller M is a prefix of
