@@ -90,15 +90,74 @@ def e2m1_round(v: np.ndarray) -> np.ndarray:
     return (mag | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
 
 
-def shared_exponent(amax: np.ndarray) -> np.ndarray:
-    """OCP MX scale exponent of a block: floor(log2 amax) - 2, clamped to
-    [-127, 127]; amax == 0 gives -127.  floor(log2) is read exactly from the
+def shared_exponent(amax: np.ndarray, emax: int = E2M1_MAX_EXP) -> np.ndarray:
+    """OCP MX scale exponent of a block: floor(log2 amax) - emax (emax: the
+    largest exponent of the element format, 2 for E2M1, 8 for E4M3), clamped
+    to [-127, 127]; amax == 0 gives -127.  floor(log2) is read exactly from the
     binary exponent (frexp), never from a rounded logarithm."""
     amax = np.asarray(amax, dtype=np.float64)
     _, ex = np.frexp(amax)  # amax = mant * 2**ex with mant in [0.5, 1)
-    e = (ex.astype(np.int64) - 1) - E2M1_MAX_EXP
+    e = (ex.astype(np.int64) - 1) - emax
     e = np.where(amax == 0.0, -127, e)
     return np.clip(e, -127, 127)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (E4M3) elements, for the W4A8 setting of the pages
+# ---------------------------------------------------------------------------
+# The pages report a W4A8 configuration (MXFP8 activations with MXFP4 weights)
+# [nubint.ai review, Table 2; en.papernotes.org, Experiments] without defining
+# the element format; it is the OCP MX v1.0 E4M3 format: sign, 4 exponent bits
+# (bias 7), 3 mantissa bits, subnormals at exponent field 0, no infinities,
+# S.1111.111 is NaN, largest finite value 448 = 1.75 * 2**8.
+
+E4M3_MAX_EXP = 8
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """Code (0..255) -> value in fp64 (NaN for S.1111.111)."""
+    c = np.asarray(code).astype(np.int64)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+#: The 127 finite non-negative E4M3 values, in code order (codes 0..126).
+E4M3_GRID = e4m3_decode(np.arange(127))
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values (already divided by the block scale) to E4M3 codes:
+    the nearest finite grid value, ties to the even code, magnitudes from 448
+    upward saturate to 448; the sign bit is kept (so -0 is code 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    m = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(E4M3_GRID, m, side="left")  # first grid value >= m
+    hi = np.clip(hi, 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = m - E4M3_GRID[lo]
+    d_hi = E4M3_GRID[hi] - m
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(E4M3_GRID[hi] == m, hi, np.where(take_hi, hi, lo))
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+#: Element formats of the MX quantiser: largest exponent and the names of the
+#: rounding and decoding functions (looked up at call time).
+_FORMATS = {
+    "e2m1": (E2M1_MAX_EXP, "e2m1_round", "e2m1_decode"),
+    "e4m3": (E4M3_MAX_EXP, "e4m3_round", "e4m3_decode"),
+}
+
+
+def element_format(fmt: str):
+    """(largest exponent, rounding function, decoding function) of ``fmt``."""
+    emax, rnd, dec = _FORMATS[fmt]
+    g = globals()
+    return emax, g[rnd], g[dec]
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
@@ -116,10 +175,10 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequantize(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
-    """MXFP4 -> fp64: element value times 2^(byte - 127) of its 32-block."""
+def dequantize(codes: np.ndarray, scale_bytes: np.ndarray, fmt: str = "e2m1") -> np.ndarray:
+    """MX codes -> fp64: element value times 2^(byte - 127) of its 32-block."""
     rows, K = codes.shape
-    vals = e2m1_decode(codes).reshape(rows, K // BLOCK, BLOCK)
+    vals = element_format(fmt)[2](codes).reshape(rows, K // BLOCK, BLOCK)
     sc = np.ldexp(1.0, np.asarray(scale_bytes, dtype=np.int64) - 127)
     return (vals * sc[..., None]).reshape(rows, K)
 
@@ -201,8 +260,10 @@ def _broadcast_ratio(r: Optional[np.ndarray], rows: int, nb: int) -> np.ndarray:
     return np.broadcast_to(r, (rows, nb)) if r.ndim == 1 else r
 
 
-def clip_and_quantize(Y32: np.ndarray, r_hi: Optional[np.ndarray], r_lo: Optional[np.ndarray]):
-    """Clip every 32-block of fp32 values and quantise it to MXFP4.
+def clip_and_quantize(Y32: np.ndarray, r_hi: Optional[np.ndarray], r_lo: Optional[np.ndarray],
+                      fmt: str = "e2m1"):
+    """Clip every 32-block of fp32 values and quantise it to MXFP4 (``fmt``
+    "e2m1") or MXFP8 ("e4m3").
 
     Returns (codes uint8 [rows, K], scale bytes uint8 [rows, K/32], z fp32).
     r_hi, r_lo: fp32 ratios, shape [K/32] (shared over rows) or [rows, K/32];
@@ -220,9 +281,10 @@ def clip_and_quantize(Y32: np.ndarray, r_hi: Optional[np.ndarray], r_lo: Optiona
     l = (rl * lo).astype(np.float32)
     z = np.minimum(np.maximum(yb, l[..., None]), u[..., None])
     amax = np.abs(z).max(axis=2)
-    e = shared_exponent(amax)
+    emax, rnd, _ = element_format(fmt)
+    e = shared_exponent(amax, emax)
     v = np.ldexp(z.astype(np.float64), -e[..., None])  # exact
-    codes = e2m1_round(v).reshape(rows, K)
+    codes = rnd(v).reshape(rows, K)
     scales = (e + 127).astype(np.uint8)
     return codes, scales, z.reshape(rows, K)
 
@@ -265,7 +327,7 @@ def _interval_abs(lo: np.ndarray, hi: np.ndarray):
     return a_lo, a_hi
 
 
-def decisions(Y64: np.ndarray, S: np.ndarray, r_hi, r_lo, exact: bool = False) -> Decisions:
+def decisions(Y64: np.ndarray, S: np.ndarray, r_hi, r_lo, exact: bool = False, fmt: str = "e2m1") -> Decisions:
     """Quantise the fp64 transform result and mark every decision that an fp32
     evaluation of it may take the other way.
 
@@ -284,7 +346,8 @@ def decisions(Y64: np.ndarray, S: np.ndarray, r_hi, r_lo, exact: bool = False) -
     rows, K = Y64.shape
     nb = K // BLOCK
     Y32 = Y64.astype(np.float32)
-    codes, scales, z32 = clip_and_quantize(Y32, r_hi, r_lo)
+    codes, scales, z32 = clip_and_quantize(Y32, r_hi, r_lo, fmt)
+    emax, rnd, _ = element_format(fmt)
     zero_sign_free = (np.asarray(S) == 0.0)
     if exact:
         f = np.zeros((rows, K), dtype=bool)
@@ -305,12 +368,12 @@ def decisions(Y64: np.ndarray, S: np.ndarray, r_hi, r_lo, exact: bool = False) -
     z_lo = np.minimum(np.maximum(y_lo, l_lo[..., None]), u_lo[..., None])
     z_hi = np.minimum(np.maximum(y_hi, l_hi[..., None]), u_hi[..., None])
     a_lo, a_hi = _interval_abs(z_lo, z_hi)
-    e_lo = shared_exponent(a_lo.max(axis=2))
-    e_hi = shared_exponent(a_hi.max(axis=2))
+    e_lo = shared_exponent(a_lo.max(axis=2), emax)
+    e_hi = shared_exponent(a_hi.max(axis=2), emax)
     block_free = e_lo != e_hi
     e = e_hi
-    c_lo = e2m1_round(np.ldexp(z_lo, -e[..., None]))
-    c_hi = e2m1_round(np.ldexp(z_hi, -e[..., None]))
+    c_lo = rnd(np.ldexp(z_lo, -e[..., None]))
+    c_hi = rnd(np.ldexp(z_hi, -e[..., None]))
     elem_free = (c_lo != c_hi).reshape(rows, K) & ~zero_sign_free
     return Decisions(codes, scales, block_free, elem_free, zero_sign_free, Y64, z32)
 
@@ -328,9 +391,10 @@ def bf16_values(bits: np.ndarray) -> np.ndarray:
 
 def act_transform_quant(X_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
                         alpha: Optional[np.ndarray], beta: Optional[np.ndarray],
-                        exact: bool = False) -> Decisions:
+                        exact: bool = False, fmt: str = "e2m1") -> Decisions:
     """Online activation path: y_b = x_b P_i, clip with sigmoid(alpha_i) * max and
-    sigmoid(beta_i) * min (no clipping when the logits are None), MXFP4 quantise
+    sigmoid(beta_i) * min (no clipping when the logits are None), MX quantise:
+    MXFP4 (``fmt`` "e2m1", the W4A4 path) or MXFP8 ("e4m3", the W4A8 setting)
     [en.papernotes.org, A Worked Example; Key Designs §1-§3]."""
     if (alpha is None) != (beta is None):
         raise ValueError("alpha and beta must both be given or both be None")
@@ -340,7 +404,7 @@ def act_transform_quant(X_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
     S = transform_abs_sum(X, P)
     rh = None if alpha is None else clip_ratio(alpha)
     rl = None if beta is None else clip_ratio(beta)
-    return decisions(Y, S, rh, rl, exact=exact)
+    return decisions(Y, S, rh, rl, exact=exact, fmt=fmt)
 
 
 def weight_prep(W_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
@@ -358,20 +422,22 @@ def weight_prep(W_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
     return decisions(Y, S, rh, rl, exact=exact)
 
 
-def gemm(xq_codes: np.ndarray, xs: np.ndarray, wq_codes: np.ndarray, ws: np.ndarray) -> np.ndarray:
+def gemm(xq_codes: np.ndarray, xs: np.ndarray, wq_codes: np.ndarray, ws: np.ndarray,
+         x_fmt: str = "e2m1") -> np.ndarray:
     """Y = deq(Xq) deq(Wq)^T in fp64 [en.papernotes.org, Key Designs §1: the
-    product Q(XP) Q(P^-1 W^T)]."""
-    return dequantize(xq_codes, xs) @ dequantize(wq_codes, ws).T
+    product Q(XP) Q(P^-1 W^T)]; the activation codes are MXFP4 or, for W4A8,
+    MXFP8 (``x_fmt`` "e4m3"); weights are MXFP4."""
+    return dequantize(xq_codes, xs, x_fmt) @ dequantize(wq_codes, ws).T
 
 
-def gemm_abs(xq_codes, xs, wq_codes, ws) -> np.ndarray:
+def gemm_abs(xq_codes, xs, wq_codes, ws, x_fmt: str = "e2m1") -> np.ndarray:
     """sum_k |x_k w_k| for every output: the scale of fp32 accumulation error."""
-    return np.abs(dequantize(xq_codes, xs)) @ np.abs(dequantize(wq_codes, ws)).T
+    return np.abs(dequantize(xq_codes, xs, x_fmt)) @ np.abs(dequantize(wq_codes, ws)).T
 
 
-def gemm_rows_cols(xq_codes, xs, wq_codes, ws, rows, cols):
+def gemm_rows_cols(xq_codes, xs, wq_codes, ws, rows, cols, x_fmt: str = "e2m1"):
     """Sampled outputs Y[rows][:, cols] and their abs-sums, one by one."""
-    Xd = dequantize(xq_codes[rows], xs[rows])
+    Xd = dequantize(xq_codes[rows], xs[rows], x_fmt)
     Wd = dequantize(wq_codes[cols], ws[cols])
     return Xd @ Wd.T, np.abs(Xd) @ np.abs(Wd).T
 

@@ -505,3 +505,87 @@ def test_hadamard_factor_recipe_is_the_block_rotation():
         P = ob.block_matrices(A, B)
         assert P.shape == (2, 32, 32)
         assert np.allclose(P[1], scipy.linalg.hadamard(32) / math.sqrt(32), atol=1e-6)
+
+
+# ------------------------------------------------ MXFP8 (E4M3), W4A8 setting
+
+
+def _e4m3_grid_by_construction():
+    """All finite non-negative E4M3 values, built from the format's fields (not
+    from the oracle): subnormals m 2^-9, normals (8 + m) 2^(E - 10); the top
+    mantissa of the top exponent is NaN."""
+    vals = [m * 2.0 ** -9 for m in range(8)]
+    for E in range(1, 16):
+        for m in range(8):
+            if E == 15 and m == 7:
+                continue
+            vals.append((8 + m) * 2.0 ** (E - 10))
+    return np.array(vals)
+
+
+def test_e4m3_decode_matches_the_format_definition():
+    g = _e4m3_grid_by_construction()
+    assert len(g) == 127 and np.all(np.diff(g) > 0)
+    assert np.array_equal(ob.e4m3_decode(np.arange(127)), g)
+    assert np.array_equal(ob.e4m3_decode(np.arange(128, 255)), -g)
+    # landmarks of the OCP E4M3 format
+    assert ob.e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9
+    assert ob.e4m3_decode(np.array([0x08]))[0] == 2.0 ** -6
+    assert ob.e4m3_decode(np.array([0x38]))[0] == 1.0
+    assert ob.e4m3_decode(np.array([0x7E]))[0] == 448.0
+    assert np.isnan(ob.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+
+
+def test_e4m3_round_equals_brute_force_nearest():
+    """Nearest of the 127 grid values by exhaustive argmin, ties to the even
+    code, saturation at 448, on random values and on every midpoint +-1 ulp."""
+    g = _e4m3_grid_by_construction()
+    rng = np.random.default_rng(8)
+    mids = (g[1:] + g[:-1]) / 2
+    v = np.concatenate([rng.uniform(0, 520, 4000), np.exp(rng.uniform(-12, 6.5, 4000)),
+                        mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), g, [0.0, 448.0, 460.0, 1e6]])
+    d = np.abs(g[None, :] - np.minimum(v, 448.0)[:, None])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among equally near values take the even code
+    want = np.where(cand.sum(axis=1) > 1, np.argmax(cand & (np.arange(127) % 2 == 0), axis=1), np.argmax(cand, axis=1))
+    assert np.array_equal(ob.e4m3_round(v), want.astype(np.uint8))
+    assert np.array_equal(ob.e4m3_round(-v), (want | 0x80).astype(np.uint8))
+    assert ob.e4m3_round(np.array([-0.0]))[0] == 0x80
+
+
+def test_mxfp8_scale_rule_and_worked_block():
+    """E4M3's largest exponent is 8, so the scale puts amax / 2^e in [256, 512);
+    a block with amax 1 gets e = -8 and 1.0 -> 256 = code 0x78; a value 0.3 in
+    that block -> 76.8, whose binade [64, 128) has spacing 8 -> nearest 80
+    (= 1.25 * 2^6: exponent field 13, mantissa 2, code 0x6A)."""
+    rng = np.random.default_rng(9)
+    amax = np.exp(rng.uniform(-40, 40, 1000))
+    e = ob.shared_exponent(amax, ob.E4M3_MAX_EXP)
+    r = amax / np.ldexp(1.0, e)
+    assert np.all((r >= 256) & (r < 512))
+    y = np.zeros((1, 32), np.float32)
+    y[0, 0], y[0, 1] = 1.0, 0.3
+    codes, scales, _ = ob.clip_and_quantize(y, None, None, "e4m3")
+    assert scales[0, 0] == 127 - 8
+    assert codes[0, 0] == 0x78 and ob.e4m3_decode(np.array([0x78]))[0] == 256.0
+    assert codes[0, 1] == 0x6A and ob.e4m3_decode(np.array([0x6A]))[0] == 80.0
+
+
+def test_mxfp8_quantisation_error_is_half_an_ulp():
+    """Normal-range elements of an MXFP8 block come back within 2^-4 of their
+    value (3 mantissa bits), except the block maxima in [448, 512) that saturate;
+    MXFP8 is much finer than MXFP4 on the same block."""
+    rng = np.random.default_rng(10)
+    y = rng.standard_normal((64, 256)).astype(np.float32)
+    c8, s8, z8 = ob.clip_and_quantize(y, None, None, "e4m3")
+    d8 = ob.dequantize(c8, s8, "e4m3")
+    z = z8.astype(np.float64)
+    scale = np.repeat(np.ldexp(1.0, s8.astype(np.int64) - 127), 32, axis=1)
+    v = np.abs(z) / scale
+    normal = (v >= 2.0 ** -6) & (v <= 448.0)
+    assert np.all(np.abs(d8 - z)[normal] <= 2.0 ** -4 * np.abs(z)[normal])
+    sat = v > 448.0  # a block maximum in [448, 512) saturates to 448
+    assert sat.any() and np.all(np.abs(d8)[sat] == 448.0 * scale[sat])
+    c4, s4, _ = ob.clip_and_quantize(y, None, None, "e2m1")
+    assert np.abs(ob.dequantize(c4, s4) - z).mean() > 3 * np.abs(d8 - z).mean()

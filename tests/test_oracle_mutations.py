@@ -39,7 +39,7 @@ def _transform_dropped_term(X, P):
     return _orig_transform(X, P2)
 
 
-def _clip_order_swapped(Y32, r_hi, r_lo):
+def _clip_order_swapped(Y32, r_hi, r_lo, fmt="e2m1"):
     Y32 = np.asarray(Y32, dtype=np.float32)
     rows, K = Y32.shape
     nb = K // 32
@@ -49,13 +49,14 @@ def _clip_order_swapped(Y32, r_hi, r_lo):
     u = (rh * yb.max(axis=2)).astype(np.float32)
     l = (rl * yb.min(axis=2)).astype(np.float32)
     z = np.maximum(np.minimum(yb, u[..., None]), l[..., None])  # min first: wrong
-    e = ob.shared_exponent(np.abs(z).max(axis=2))
-    codes = ob.e2m1_round(np.ldexp(z.astype(np.float64), -e[..., None])).reshape(rows, K)
+    emax, rnd, _ = ob.element_format(fmt)
+    e = ob.shared_exponent(np.abs(z).max(axis=2), emax)
+    codes = rnd(np.ldexp(z.astype(np.float64), -e[..., None])).reshape(rows, K)
     return codes, (e + 127).astype(np.uint8), z.reshape(rows, K)
 
 
-def _clip_ratios_swapped(Y32, r_hi, r_lo):
-    return _orig_clip(Y32, r_lo, r_hi)
+def _clip_ratios_swapped(Y32, r_hi, r_lo, fmt="e2m1"):
+    return _orig_clip(Y32, r_lo, r_hi, fmt)
 
 
 def _round_ties_away(v):
@@ -79,14 +80,14 @@ def _round_unsigned_zero(v):
     return np.where((codes & 7) == 0, 0, codes).astype(np.uint8)
 
 
-def _exponent_off_by_one(amax):
-    return np.clip(_orig_exp(amax) + 1, -127, 127)
+def _exponent_off_by_one(amax, emax=2):
+    return np.clip(_orig_exp(amax, emax) + 1, -127, 127)
 
 
-def _exponent_via_log2(amax):
+def _exponent_via_log2(amax, emax=2):
     amax = np.asarray(amax, dtype=np.float64)
     with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(amax.astype(np.float32))).astype(np.int64) - 2
+        e = np.floor(np.log2(amax.astype(np.float32))).astype(np.int64) - emax
     return np.clip(np.where(amax == 0, -127, e), -127, 127)
 
 
@@ -95,13 +96,13 @@ def _pack_high_nibble_first(codes):
     return (c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8)
 
 
-def _dequantize_scale_dropped(codes, scale_bytes):
-    return ob.e2m1_decode(codes)
+def _dequantize_scale_dropped(codes, scale_bytes, fmt="e2m1"):
+    return ob.element_format(fmt)[2](codes)
 
 
-def _dequantize_scale_sign(codes, scale_bytes):
+def _dequantize_scale_sign(codes, scale_bytes, fmt="e2m1"):
     rows, K = codes.shape
-    vals = ob.e2m1_decode(codes).reshape(rows, K // 32, 32)
+    vals = ob.element_format(fmt)[2](codes).reshape(rows, K // 32, 32)
     sc = np.ldexp(1.0, 127 - np.asarray(scale_bytes, dtype=np.int64))  # wrong sign of the exponent
     return (vals * sc[..., None]).reshape(rows, K)
 
@@ -116,6 +117,22 @@ def _sigmoid_wrong_sign(logits):
     return (1.0 / (1.0 + np.exp(x))).astype(np.float32)
 
 
+def _e4m3_ties_up(v):
+    v = np.asarray(v, dtype=np.float64)
+    m = np.minimum(np.abs(v), ob.E4M3_MAX)
+    g = ob.E4M3_GRID
+    code = np.clip(np.searchsorted(g, m, side="right") - 1, 0, 126)
+    nxt = np.clip(code + 1, 0, 126)
+    code = np.where(m - g[code] >= g[nxt] - m, nxt, code)  # ties upward: wrong
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def _e4m3_no_subnormals(v):
+    codes = _orig_e4m3(v)
+    return np.where((codes & 0x78) == 0, codes & 0x80, codes).astype(np.uint8)  # flush to zero
+
+
+_orig_e4m3 = _orig("e4m3_round")
 _orig_transform = _orig("transform")
 _orig_clip = _orig("clip_and_quantize")
 _orig_round = _orig("e2m1_round")
@@ -151,6 +168,12 @@ CASES = {
                                               [T.test_kron_inverse_identity,
                                                T.test_linear_layer_equivalence_without_quantisation]),
     "sigmoid sign flipped": ("clip_ratio", _sigmoid_wrong_sign, [T.test_clip_ratio_matches_library_sigmoid]),
+    "E4M3 ties rounded upward": ("e4m3_round", _e4m3_ties_up,
+                                 [T.test_e4m3_round_equals_brute_force_nearest, T.test_mxfp8_scale_rule_and_worked_block]),
+    "E4M3 subnormals flushed": ("e4m3_round", _e4m3_no_subnormals, [T.test_e4m3_round_equals_brute_force_nearest]),
+    "E4M3 largest exponent taken as 7": ("shared_exponent",
+                                         lambda amax, emax=2: _orig_exp(amax, 7 if emax == 8 else emax),
+                                         [T.test_mxfp8_scale_rule_and_worked_block]),
 }
 
 
