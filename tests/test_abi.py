@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("batq_act_transform_quant", "batq_weight_prep", "batq_mxfp4_gemm", "batq_gpk_invert",
               "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
-              "batq_weight_pack", "batq_mxfp4_gemm_packed"):
+              "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
+              "batq_mxfp8_gemm_packed"):
         assert n in names
 
 
@@ -54,7 +55,7 @@ def _tq(lib, fn, x=FAKE, M=4, K=64, ld=64, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0,
     return getattr(lib, fn)(x, M, K, ld, a, b, A, B, rh, rl, q, s, None)
 
 
-@pytest.mark.parametrize("fn", ["batq_act_transform_quant", "batq_weight_prep"])
+@pytest.mark.parametrize("fn", ["batq_act_transform_quant", "batq_weight_prep", "batq_act_transform_quant_mxfp8"])
 def test_transform_argument_checks(lib, fn):
     assert _tq(lib, fn, x=0) == NULL
     assert _tq(lib, fn, A=0) == NULL
@@ -107,8 +108,9 @@ def test_pack_argument_checks(lib):
     assert f(FAKE, FAKE, 0, 256, FAKE, None) == OK
 
 
-def test_packed_gemm_argument_checks(lib):
-    f = lib.batq_mxfp4_gemm_packed
+@pytest.mark.parametrize("name", ["batq_mxfp4_gemm_packed", "batq_mxfp8_gemm_packed"])
+def test_packed_gemm_argument_checks(lib, name):
+    f = getattr(lib, name)
     assert f(FAKE, FAKE, FAKE, 4, 4, 288, FAKE, 0, None) == SHAPE
     assert f(FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 0, None) == SHAPE
     assert f(FAKE, FAKE, FAKE, 4, -1, 256, FAKE, 0, None) == SHAPE

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     library_path,
     mxfp4_gemm,
     mxfp4_gemm_packed,
+    mxfp8_gemm_packed,
+    act_transform_quant_mxfp8,
     PackedWeight,
     weight_pack,
     weight_packed_bytes,

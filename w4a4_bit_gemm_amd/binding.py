@@ -62,6 +62,11 @@ def _load():
     lib.batq_weight_pack.argtypes = [P, P, I64, I64, P, P]
     lib.batq_mxfp4_gemm_packed.restype = ctypes.c_int
     lib.batq_mxfp4_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    lib.batq_act_transform_quant_mxfp8.restype = ctypes.c_int
+    lib.batq_act_transform_quant_mxfp8.argtypes = [P, I64, I64, I64, ctypes.c_int32, ctypes.c_int32, P, P, P, P,
+                                                    P, P, P]
+    lib.batq_mxfp8_gemm_packed.restype = ctypes.c_int
+    lib.batq_mxfp8_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
     _lib = lib
     return lib
 
@@ -128,6 +133,16 @@ def act_transform_quant(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple] = No
     X: [M, K] bf16; A: [a, a] f32; B: [K/32, b, b] f32; r_hi, r_lo: [K/32] f32
     ratios or None (no clip).  Returns (Xq uint8 [M, K/2], Xs uint8 [M, K/32]).
     """
+    return _act(X, A, B, r_hi, r_lo, out, fp8=False)
+
+
+def act_transform_quant_mxfp8(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple] = None):
+    """The same transform and clipping with MXFP8 (E4M3) output, the W4A8
+    setting.  Returns (Xq8 uint8 [M, K], Xs uint8 [M, K/32])."""
+    return _act(X, A, B, r_hi, r_lo, out, fp8=True)
+
+
+def _act(X, A, B, r_hi, r_lo, out, fp8: bool):
     torch = _torch()
     _req(X, torch.bfloat16, "X")
     _req(A, torch.float32, "A")
@@ -142,12 +157,13 @@ def act_transform_quant(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple] = No
     if B.shape[0] != K // 32 or (r_hi is not None and r_hi.numel() != K // 32):
         raise ValueError("B / ratio shapes must match K/32 blocks")
     if out is None:
-        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+        Xq = torch.empty((M, K if fp8 else K // 2), dtype=torch.uint8, device=X.device)
         Xs = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
     else:
         Xq, Xs = out
-    st = _load().batq_act_transform_quant(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi),
-                                          _ptr(r_lo), _ptr(Xq), _ptr(Xs), _stream_ptr(torch, X.device))
+    fn = _load().batq_act_transform_quant_mxfp8 if fp8 else _load().batq_act_transform_quant
+    st = fn(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Xq), _ptr(Xs),
+            _stream_ptr(torch, X.device))
     _check(st)
     return Xq, Xs
 
@@ -276,5 +292,28 @@ def mxfp4_gemm_packed(Xq, Xs, Wp: PackedWeight, out_dtype=None, out=None):
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
     st = _load().batq_mxfp4_gemm_packed(_ptr(Xq), _ptr(Xs), _ptr(Wp.data), M, N, K, _ptr(out), code,
                                         _stream_ptr(torch, Xq.device))
+    _check(st)
+    return out
+
+
+def mxfp8_gemm_packed(Xq8, Xs, Wp: PackedWeight, out_dtype=None, out=None):
+    """W4A8: Y = deq8(Xq8, Xs) deq4(W)^T with W packed by :func:`weight_pack`
+    and MXFP8 (E4M3) activation codes from :func:`act_transform_quant_mxfp8`."""
+    torch = _torch()
+    _req(Xq8, torch.uint8, "Xq8")
+    _req(Xs, torch.uint8, "Xs")
+    M, K = Xq8.shape
+    if K != Wp.K or tuple(Xs.shape) != (M, K // 32):
+        raise ValueError("operand shapes do not match")
+    N = Wp.N
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=Xq8.device)
+    else:
+        _req(out, out_dtype, "out")
+    code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    st = _load().batq_mxfp8_gemm_packed(_ptr(Xq8), _ptr(Xs), _ptr(Wp.data), M, N, K, _ptr(out), code,
+                                        _stream_ptr(torch, Xq8.device))
     _check(st)
     return out

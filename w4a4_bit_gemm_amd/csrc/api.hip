@@ -80,7 +80,7 @@ batq_status check_transform_args(const void* x, int64_t rows, int64_t K, int64_t
 
 batq_status run_transform(const void* x, int64_t rows, int64_t K, int64_t ld, int32_t a, const float* A,
                           const float* B, const float* r_hi, const float* r_lo, int64_t r_ld, uint8_t* q,
-                          uint8_t* s, hipStream_t stream) {
+                          uint8_t* s, hipStream_t stream, int fp8 = 0) {
   if (rows == 0) return BATQ_OK;
   batq::TransformQuantArgs args;
   args.x = static_cast<const uint16_t*>(x);
@@ -95,6 +95,7 @@ batq_status run_transform(const void* x, int64_t rows, int64_t K, int64_t ld, in
   args.r_ld = r_ld;
   args.q = q;
   args.s = s;
+  args.fp8 = fp8;
   return batq::launch_transform_quant(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 
@@ -206,6 +207,36 @@ batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const u
   args.y = Y;
   args.out_f32 = (out == BATQ_OUT_F32);
   args.vec_store = aligned(Y, 16) && (N % (args.out_f32 ? 4 : 8) == 0);
+  return batq::launch_mxfp4_gemm_packed(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
+}
+
+batq_status batq_act_transform_quant_mxfp8(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a,
+                                           int32_t b, const float* A, const float* B, const float* r_hi,
+                                           const float* r_lo, uint8_t* Xq8, uint8_t* Xs, hipStream_t stream) {
+  const batq_status st = check_transform_args(X_bf16, M, K, ldx, a, b, A, B, r_hi, r_lo, Xq8, Xs);
+  if (st != BATQ_OK) return st;
+  return run_transform(X_bf16, M, K, ldx, a, A, B, r_hi, r_lo, 0, Xq8, Xs, stream, 1);
+}
+
+batq_status batq_mxfp8_gemm_packed(const uint8_t* Xq8, const uint8_t* Xs, const uint8_t* Wp, int64_t M, int64_t N,
+                                   int64_t K, void* Y, batq_out_dtype out, hipStream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 256 != 0) return BATQ_ERR_SHAPE;
+  if (out != BATQ_OUT_BF16 && out != BATQ_OUT_F32) return BATQ_ERR_UNSUPPORTED;
+  if (Xq8 == nullptr || Xs == nullptr || Wp == nullptr || Y == nullptr) return BATQ_ERR_NULL;
+  if (!aligned(Xq8, 16) || !aligned(Xs, 16) || !aligned(Wp, 16) || !aligned(Y, 4)) return BATQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return BATQ_OK;
+  batq::GemmArgs args;
+  args.xq = Xq8;
+  args.xs = Xs;
+  args.wq = Wp;
+  args.ws = nullptr;
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.y = Y;
+  args.out_f32 = (out == BATQ_OUT_F32);
+  args.vec_store = aligned(Y, 16) && (N % (args.out_f32 ? 4 : 8) == 0);
+  args.a_fp8 = 1;
   return batq::launch_mxfp4_gemm_packed(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 

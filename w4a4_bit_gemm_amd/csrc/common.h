@@ -36,8 +36,9 @@ struct TransformQuantArgs {
   const float* r_hi;    // clip ratios or nullptr (no clipping)
   const float* r_lo;
   int64_t r_ld;         // ratio index = row * r_ld + block (0: shared over rows)
-  uint8_t* q;           // [rows][K/2]
+  uint8_t* q;           // [rows][K/2] (E2M1) or [rows][K] (E4M3)
   uint8_t* s;           // [rows][K/32]
+  int fp8 = 0;          // 1: MXFP8 (E4M3) codes instead of MXFP4 (E2M1)
 };
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream);
 
@@ -50,6 +51,7 @@ struct GemmArgs {
   void* y;
   int out_f32;
   int vec_store;  // Y 16-byte aligned and rows a whole number of 16-byte chunks
+  int a_fp8 = 0;  // packed GEMM only: xq holds E4M3 codes [M][K] (W4A8) instead of E2M1 [M][K/2]
 };
 hipError_t launch_mxfp4_gemm(const GemmArgs& args, hipStream_t stream);
 

@@ -53,6 +53,18 @@ __device__ __forceinline__ f32x16 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(a), op(b), acc, 4, 4, J, (int)sa, J, (int)sb);
 }
 
+// E4M3 activations x E2M1 weights (the W4A8 setting).  The E4M3 operand of a
+// lane (row r, half g) is 32 bytes: k = 16 g .. 16 g + 15 of the 64-k step in
+// bytes 0..15 and k = 32 + 16 g .. 32 + 16 g + 15 in bytes 16..31, while the
+// E2M1 operand keeps 32 consecutive k per lane half; each lane's scale byte
+// covers the 32-k block of its half (all checked on the device).
+template <int J>
+__device__ __forceinline__ f32x16 mfma_fp8_fp4(uint4 alo, uint4 ahi, uint4 b, uint32_t sa, uint32_t sb,
+                                               f32x16 acc) {
+  const i32x8 a = {(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op(b), acc, 0, 4, J, (int)sa, J, (int)sb);
+}
+
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -128,26 +140,44 @@ __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_
     n##_10 = ld16(s1_); n##_11 = ld16(s1_ + 1024); n##_12 = ld16(s1_ + 2048); n##_13 = ld16(s1_ + 3072); \
     n##_s1 = ld4(s1_ + 4096 - 12 * lane);                                                      \
   }
-#define BATQ_DECL_A(n) uint4 n##_0, n##_1, n##_2, n##_3; uint32_t n##_s;
+#define BATQ_DECL_A(n) uint4 n##_0, n##_1, n##_2, n##_3, n##_4, n##_5, n##_6, n##_7; uint32_t n##_s;
 // activation stage ST -> set n: thread owns code chunks id = tid + 256 i
-// (row id / 8, chunk id % 8) and scale dword (row tid / 2, half tid % 2)
+// (E2M1: row id / 8, chunk id % 8, i < 4; E4M3: row id / 16, chunk id % 16,
+// i < 8) and scale dword (row tid / 2, half tid % 2)
 #define BATQ_LOAD_A(n, ST)                                                                     \
   {                                                                                            \
     const int64_t st_ = opaque_stage(ST);                                                      \
-    const int64_t off_ = st_ * kRowBytes;                                                      \
+    const int64_t off_ = st_ * kARow;                                                          \
     n##_0 = ld16(a_base0 + off_);                                                              \
     n##_1 = ld16(a_base1 + off_);                                                              \
     n##_2 = ld16(a_base2 + off_);                                                              \
     n##_3 = ld16(a_base3 + off_);                                                              \
+    if constexpr (A8) {                                                                        \
+      n##_4 = ld16(a_base4 + off_);                                                            \
+      n##_5 = ld16(a_base5 + off_);                                                            \
+      n##_6 = ld16(a_base6 + off_);                                                            \
+      n##_7 = ld16(a_base7 + off_);                                                            \
+    }                                                                                          \
     if (!GS) n##_s = ld4(a_sbase + 8 * st_);                                                   \
   }
 #define BATQ_STORE_A(n, SLOT)                                                                  \
   {                                                                                            \
-    a_dst(SLOT, tid)[0] = n##_0;                                                               \
-    a_dst(SLOT, tid + 256)[0] = n##_1;                                                         \
-    a_dst(SLOT, tid + 512)[0] = n##_2;                                                         \
-    a_dst(SLOT, tid + 768)[0] = n##_3;                                                         \
-    if (!GS) *reinterpret_cast<uint32_t*>((SLOT) + kAStage + 4 * tid) = n##_s;                 \
+    if constexpr (A8) {                                                                        \
+      a_dst8(SLOT, tid)[0] = n##_0;                                                            \
+      a_dst8(SLOT, tid + 256)[0] = n##_1;                                                      \
+      a_dst8(SLOT, tid + 512)[0] = n##_2;                                                      \
+      a_dst8(SLOT, tid + 768)[0] = n##_3;                                                      \
+      a_dst8(SLOT, tid + 1024)[0] = n##_4;                                                     \
+      a_dst8(SLOT, tid + 1280)[0] = n##_5;                                                     \
+      a_dst8(SLOT, tid + 1536)[0] = n##_6;                                                     \
+      a_dst8(SLOT, tid + 1792)[0] = n##_7;                                                     \
+    } else {                                                                                   \
+      a_dst(SLOT, tid)[0] = n##_0;                                                             \
+      a_dst(SLOT, tid + 256)[0] = n##_1;                                                       \
+      a_dst(SLOT, tid + 512)[0] = n##_2;                                                       \
+      a_dst(SLOT, tid + 768)[0] = n##_3;                                                       \
+    }                                                                                          \
+    if (!GS) *reinterpret_cast<uint32_t*>((SLOT) + kAStg + 4 * tid) = n##_s;                   \
   }
 // Grouped activation scales (GS): group G = stages 4G .. 4G+3.  Thread
 // (row tid / 2, half h = tid % 2) loads the 16 bytes of stages 4G + 2h and
@@ -177,6 +207,22 @@ __device__ __forceinline__ uint4* a_dst(uint8_t* slot, int id) {
   const int row = id >> 3;
   return reinterpret_cast<uint4*>(slot + row * kRowBytes + 16 * ((id & 7) ^ swz(row)));
 }
+// E4M3 activations: 256-byte rows (one stage), 16-byte chunk c of row r at
+// position c ^ (r % 16): the MMA's reads of one chunk over 16 consecutive
+// rows hit 16 different bank groups.
+constexpr int kRowBytes8 = 256;
+__device__ __forceinline__ const uint8_t* a_row_base8(const GemmArgs& p, int64_t m0, int id) {
+  int64_t gr = m0 + (id >> 4);
+  gr = gr < p.M ? gr : p.M - 1;
+  return p.xq + gr * p.K + 16 * (id & 15);
+}
+__device__ __forceinline__ uint4* a_dst8(uint8_t* slot, int id) {
+  const int row = id >> 4;
+  return reinterpret_cast<uint4*>(slot + row * kRowBytes8 + 16 * ((id & 15) ^ (row & 15)));
+}
+__device__ __forceinline__ uint4 lds_frag8(const uint8_t* base, int row, int chunk) {
+  return *reinterpret_cast<const uint4*>(base + row * kRowBytes8 + 16 * (chunk ^ (row & 15)));
+}
 
 __device__ __forceinline__ uint4 lds_frag(const uint8_t* base, int row, int chunk) {
   return *reinterpret_cast<const uint4*>(base + row * kRowBytes + 16 * (chunk ^ swz(row)));
@@ -197,6 +243,29 @@ __device__ __forceinline__ void read_a(const uint8_t* As, int j, uint4 (&fa)[kMT
   for (int i = 0; i < kMT; ++i) fa[i] = lds_frag(As, 32 * i + r32, 4 * g + j);
 }
 
+// E4M3 fragments of sub-step J into the named registers P##l0..3 / P##h0..3:
+// half g of MX blocks J and 4 + J of the stage (16-byte chunks 2 J + g and
+// 8 + 2 J + g of the row).  Named scalars, not arrays: arrays of vectors here
+// end up in scratch.
+#define BATQ_RD8(SLOT, J, P)                                                                   \
+  P##l0 = lds_frag8(SLOT, r32, 2 * (J) + g);                                                   \
+  P##h0 = lds_frag8(SLOT, r32, 8 + 2 * (J) + g);                                               \
+  P##l1 = lds_frag8(SLOT, 32 + r32, 2 * (J) + g);                                              \
+  P##h1 = lds_frag8(SLOT, 32 + r32, 8 + 2 * (J) + g);                                          \
+  P##l2 = lds_frag8(SLOT, 64 + r32, 2 * (J) + g);                                              \
+  P##h2 = lds_frag8(SLOT, 64 + r32, 8 + 2 * (J) + g);                                          \
+  P##l3 = lds_frag8(SLOT, 96 + r32, 2 * (J) + g);                                              \
+  P##h3 = lds_frag8(SLOT, 96 + r32, 8 + 2 * (J) + g);
+#define BATQ_MM8(J, P, B0, B1, BS0, BS1)                                                       \
+  acc[0][0] = mfma_fp8_fp4<J>(P##l0, P##h0, B0, sa_[0], BS0, acc[0][0]);                       \
+  acc[0][1] = mfma_fp8_fp4<J>(P##l0, P##h0, B1, sa_[0], BS1, acc[0][1]);                       \
+  acc[1][0] = mfma_fp8_fp4<J>(P##l1, P##h1, B0, sa_[1], BS0, acc[1][0]);                       \
+  acc[1][1] = mfma_fp8_fp4<J>(P##l1, P##h1, B1, sa_[1], BS1, acc[1][1]);                       \
+  acc[2][0] = mfma_fp8_fp4<J>(P##l2, P##h2, B0, sa_[2], BS0, acc[2][0]);                       \
+  acc[2][1] = mfma_fp8_fp4<J>(P##l2, P##h2, B1, sa_[2], BS1, acc[2][1]);                       \
+  acc[3][0] = mfma_fp8_fp4<J>(P##l3, P##h3, B0, sa_[3], BS0, acc[3][0]);                       \
+  acc[3][1] = mfma_fp8_fp4<J>(P##l3, P##h3, B1, sa_[3], BS1, acc[3][1]);
+
 // Stage from an LDS slot and a weight register set into the accumulators,
 // with the LDS reads of sub-step j+1 issued ahead of the MFMAs of sub-step j.
 #define BATQ_MMA_STAGE(SLOT, n, SCALES)                                                        \
@@ -204,29 +273,51 @@ __device__ __forceinline__ void read_a(const uint8_t* As, int j, uint4 (&fa)[kMT
     uint32_t sa_[kMT];                                                                         \
     _Pragma("unroll") for (int i = 0; i < kMT; ++i)                                            \
       sa_[i] = ld4((SCALES) + (32 * i + r32) * 8 + 4 * g);                                     \
-    uint4 fa0_[kMT], fa1_[kMT];                                                                \
-    read_a(SLOT, 0, fa0_, r32, g);                                                             \
-    read_a(SLOT, 1, fa1_, r32, g);                                                             \
-    sched_fence();                                                                             \
-    mma_sub<0>(acc, fa0_, n##_00, n##_10, n##_s0, n##_s1, sa_);                                \
-    sched_fence();                                                                             \
-    read_a(SLOT, 2, fa0_, r32, g);                                                             \
-    sched_fence();                                                                             \
-    mma_sub<1>(acc, fa1_, n##_01, n##_11, n##_s0, n##_s1, sa_);                                \
-    sched_fence();                                                                             \
-    read_a(SLOT, 3, fa1_, r32, g);                                                             \
-    sched_fence();                                                                             \
-    mma_sub<2>(acc, fa0_, n##_02, n##_12, n##_s0, n##_s1, sa_);                                \
-    sched_fence();                                                                             \
-    mma_sub<3>(acc, fa1_, n##_03, n##_13, n##_s0, n##_s1, sa_);                                \
+    if constexpr (A8) {                                                                        \
+      uint4 x0l0, x0h0, x0l1, x0h1, x0l2, x0h2, x0l3, x0h3;                                    \
+      uint4 x1l0, x1h0, x1l1, x1h1, x1l2, x1h2, x1l3, x1h3;                                    \
+      BATQ_RD8(SLOT, 0, x0)                                                                    \
+      BATQ_RD8(SLOT, 1, x1)                                                                    \
+      sched_fence();                                                                           \
+      BATQ_MM8(0, x0, n##_00, n##_10, n##_s0, n##_s1)                                          \
+      sched_fence();                                                                           \
+      BATQ_RD8(SLOT, 2, x0)                                                                    \
+      sched_fence();                                                                           \
+      BATQ_MM8(1, x1, n##_01, n##_11, n##_s0, n##_s1)                                          \
+      sched_fence();                                                                           \
+      BATQ_RD8(SLOT, 3, x1)                                                                    \
+      sched_fence();                                                                           \
+      BATQ_MM8(2, x0, n##_02, n##_12, n##_s0, n##_s1)                                          \
+      sched_fence();                                                                           \
+      BATQ_MM8(3, x1, n##_03, n##_13, n##_s0, n##_s1)                                          \
+    } else {                                                                                   \
+      uint4 fa0_[kMT], fa1_[kMT];                                                              \
+      read_a(SLOT, 0, fa0_, r32, g);                                                           \
+      read_a(SLOT, 1, fa1_, r32, g);                                                           \
+      sched_fence();                                                                           \
+      mma_sub<0>(acc, fa0_, n##_00, n##_10, n##_s0, n##_s1, sa_);                              \
+      sched_fence();                                                                           \
+      read_a(SLOT, 2, fa0_, r32, g);                                                           \
+      sched_fence();                                                                           \
+      mma_sub<1>(acc, fa1_, n##_01, n##_11, n##_s0, n##_s1, sa_);                              \
+      sched_fence();                                                                           \
+      read_a(SLOT, 3, fa1_, r32, g);                                                           \
+      sched_fence();                                                                           \
+      mma_sub<2>(acc, fa0_, n##_02, n##_12, n##_s0, n##_s1, sa_);                              \
+      sched_fence();                                                                           \
+      mma_sub<3>(acc, fa1_, n##_03, n##_13, n##_s0, n##_s1, sa_);                              \
+    }                                                                                          \
   }
 
 // NST > 0: stage count fixed at compile time, loop fully unrolled (exact
 // compiler wait counts).  NST == 0: runtime stage count.
-template <int NST, bool GS>
+// A8: E4M3 activations (W4A8) instead of E2M1.
+template <int NST, bool GS, bool A8>
 __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t slot0[GS ? kAStage : kSlot];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot1[GS ? kAStage : kSlot];
+  constexpr int kARow = A8 ? kRowBytes8 : kRowBytes;  // activation bytes per row and stage
+  constexpr int kAStg = kBM * kARow;
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[GS ? kAStg : kAStg + kAScale];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[GS ? kAStg : kAStg + kAScale];
   __shared__ __attribute__((aligned(1024))) uint8_t sgrp0[GS ? 4096 : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sgrp1[GS ? 4096 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t epi_buf[4 * kEpiWave];
@@ -273,10 +364,14 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
   // prefetches are clamped to the last stage (a clamped load re-reads an
   // L2-resident stage and is never used), keeping every step branch-free.
 #define BATQ_CL(x) ((x) < last ? (x) : last)
-  const uint8_t* const a_base0 = a_row_base(p, m0, tid);
-  const uint8_t* const a_base1 = a_row_base(p, m0, tid + 256);
-  const uint8_t* const a_base2 = a_row_base(p, m0, tid + 512);
-  const uint8_t* const a_base3 = a_row_base(p, m0, tid + 768);
+  const uint8_t* const a_base0 = A8 ? a_row_base8(p, m0, tid) : a_row_base(p, m0, tid);
+  const uint8_t* const a_base1 = A8 ? a_row_base8(p, m0, tid + 256) : a_row_base(p, m0, tid + 256);
+  const uint8_t* const a_base2 = A8 ? a_row_base8(p, m0, tid + 512) : a_row_base(p, m0, tid + 512);
+  const uint8_t* const a_base3 = A8 ? a_row_base8(p, m0, tid + 768) : a_row_base(p, m0, tid + 768);
+  const uint8_t* const a_base4 = A8 ? a_row_base8(p, m0, tid + 1024) : nullptr;
+  const uint8_t* const a_base5 = A8 ? a_row_base8(p, m0, tid + 1280) : nullptr;
+  const uint8_t* const a_base6 = A8 ? a_row_base8(p, m0, tid + 1536) : nullptr;
+  const uint8_t* const a_base7 = A8 ? a_row_base8(p, m0, tid + 1792) : nullptr;
   const uint8_t* const a_sbase = a_scale_base(p, m0, tid, 4);   // per-stage scales
   const uint8_t* const a_gbase = a_scale_base(p, m0, tid, 16);  // grouped scales
   const int64_t ngrp = nst >> 2;
@@ -288,11 +383,15 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
   BATQ_DECL_B(b0)
   BATQ_DECL_B(b1)
   BATQ_DECL_B(b2)
+  // Weights are prefetched kBDist stages ahead: two for E2M1 (three register
+  // sets), one for E4M3, whose MFMAs take twice as long per stage and whose
+  // activation fragments need the registers (two sets).
+  constexpr int kBDist = A8 ? 1 : 2;
   BATQ_LOAD_A(a0, 0)
   BATQ_LOAD_B(b0, 0)
   if (NST == 0 || NST > 1) {
     BATQ_LOAD_A(a1, BATQ_CL(1))
-    BATQ_LOAD_B(b1, BATQ_CL(1))
+    if (kBDist == 2) BATQ_LOAD_B(b1, BATQ_CL(1))
   }
   if (GS) BATQ_LOAD_AS(0)
   BATQ_STORE_A(a0, slot0)
@@ -316,10 +415,10 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
         BATQ_LOAD_AS(((S) >> 2) + 2 < ngrp ? ((S) >> 2) + 2 : ngrp - 1)                        \
     }                                                                                          \
     if (NST == 0 || (S) + 3 < NST) BATQ_LOAD_A(ANEXT, BATQ_CL((S) + 3)) /* act stage s+3 */     \
-    if (NST == 0 || (S) + 2 < NST) BATQ_LOAD_B(BPF, BATQ_CL((S) + 2))   /* weight stage s+2 */  \
+    if (NST == 0 || (S) + kBDist < NST) BATQ_LOAD_B(BPF, BATQ_CL((S) + kBDist)) /* weights */  \
     sched_fence();                                                                             \
     const uint8_t* scales_ = GS ? ((((S) >> 2) & 1) ? sgrp1 : sgrp0) + 1024 * ((J) % 4)        \
-                                : (CUR) + kAStage;                                             \
+                                : (CUR) + kAStg;                                               \
     BATQ_MMA_STAGE(CUR, BCUR, scales_)                                                         \
     __builtin_amdgcn_s_waitcnt(0xC07F);          /* lgkmcnt(0): s+1 written, s read */         \
     block_barrier();                                                                           \
@@ -334,9 +433,28 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
     case 4: BATQ_STEP(S, S, slot0, slot1, a1, b1, b0) break;                                   \
     default: BATQ_STEP(S, S, slot1, slot0, a0, b2, b1) break;                                  \
   }
+  // E4M3: weight sets alternate with period 2.
+#define BATQ_STEP4(S)                                                                          \
+  switch ((S) % 2) {                                                                           \
+    case 0: BATQ_STEP(S, S, slot0, slot1, a1, b0, b1) break;                                   \
+    default: BATQ_STEP(S, S, slot1, slot0, a0, b1, b0) break;                                  \
+  }
   if (NST > 0) {
+    if constexpr (A8) {
 #pragma unroll
-    for (int s = 0; s < NST; ++s) BATQ_STEP6(s)
+      for (int s = 0; s < NST; ++s) BATQ_STEP4(s)
+    } else {
+#pragma unroll
+      for (int s = 0; s < NST; ++s) BATQ_STEP6(s)
+    }
+  } else if constexpr (A8) {
+    // Period 4 = lcm(2 slots, 2 weight sets, 4 stages per scale group).
+    for (int64_t s = 0; s < nst; s += 4) {
+      BATQ_STEP(s, 0, slot0, slot1, a1, b0, b1)
+      if (s + 1 < nst) BATQ_STEP(s + 1, 1, slot1, slot0, a0, b1, b0)
+      if (s + 2 < nst) BATQ_STEP(s + 2, 2, slot0, slot1, a1, b0, b1)
+      if (s + 3 < nst) BATQ_STEP(s + 3, 3, slot1, slot0, a0, b1, b0)
+    }
   } else {
     // Period 12 = lcm(2 slots, 3 weight sets, 4 stages per scale group).
     for (int64_t s = 0; s < nst; s += 12) {
@@ -354,6 +472,7 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
       if (s + 11 < nst) BATQ_STEP(s + 11, 11, slot1, slot0, a0, b2, b1)
     }
   }
+#undef BATQ_STEP4
 #undef BATQ_STEP6
 #undef BATQ_STEP
 #undef BATQ_CL
@@ -407,13 +526,18 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
   }
 }
 
-template <int NST, bool GS>
-hipError_t launch_packed(const GemmArgs& args, hipStream_t stream) {
+template <int NST, bool GS, bool A8>
+hipError_t launch_packed_t(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = (int)((args.M + kBM - 1) / kBM);
   const int tiles_n = (int)((args.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((mxfp4_gemm_packed_kernel<NST, GS>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+  hipLaunchKernelGGL((mxfp4_gemm_packed_kernel<NST, GS, A8>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
                      tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+template <int NST, bool GS>
+hipError_t launch_packed(const GemmArgs& args, hipStream_t stream) {
+  return args.a_fp8 ? launch_packed_t<NST, GS, true>(args, stream) : launch_packed_t<NST, GS, false>(args, stream);
 }
 
 }  // namespace

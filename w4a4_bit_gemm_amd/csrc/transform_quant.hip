@@ -100,19 +100,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 //                     row pieces.  It never waits for its stores.
 // Per tile i, two workgroup barriers: A_i (tile i is in LDS; staging is free)
 // and B_i (tile i's codes and scales are staged).
+template <bool F8>
 struct TQSmem {
   static constexpr int kXRow = 512;        // bytes per staged bf16 row (256 channels)
   static constexpr int kX = kTT * kXRow;   // one tile slot
-  static constexpr int kQRow = 144;        // 128 code bytes + 16 pad: conflict-free 8-byte writes
+  // staged code row: 128 (E2M1) or 256 (E4M3) bytes + 16 pad, conflict-free writes
+  static constexpr int kQRow = F8 ? 272 : 144;
 };
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
 
 // PER_ROW: one ratio pair per (row, block), read per tile (the weight side);
 // otherwise one pair per block, read once (activations), which keeps every
-// memory wait out of the activations' tile loop.
-template <bool PER_ROW>
+// memory wait out of the activations' tile loop.  F8: MXFP8 (E4M3) codes, one
+// byte per element (the W4A8 setting); otherwise MXFP4 (E2M1), two per byte.
+template <bool PER_ROW, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
     TransformQuantArgs p) {
-  using T = TQSmem;
+  using T = TQSmem<F8>;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kRing * T::kX];
   __shared__ __attribute__((aligned(16))) uint8_t qs[kTT * T::kQRow];
   __shared__ __attribute__((aligned(16))) uint8_t ss[kTT * 8];
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       if (i < ntile) load_tile(i, i);
   }
   static_assert(kRing == 4, "the loader's wait distinguishes 0, 1 or 2 younger tiles");
-  const int64_t qld = p.K >> 1;
+  const int64_t qld = F8 ? p.K : (p.K >> 1);
 
   for (int64_t i = 0; i < ntile; ++i) {
     if (loader) {
@@ -269,8 +274,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const float zmax = __builtin_amdgcn_fmed3f(mx, l, u);
       const float zmin = __builtin_amdgcn_fmed3f(mn, l, u);
       const float amax = fmaxf(fabsf(zmax), fabsf(zmin));
-      // scale byte = e + 127 = max(biased exponent of amax - 2, 0)
-      const int sbyte = max((int)(__float_as_uint(amax) >> 23) - 2, 0);
+      // scale byte = e + 127 = max(biased exponent of amax - emax, 0), emax = 2
+      // for E2M1 and 8 for E4M3
+      const int sbyte = max((int)(__float_as_uint(amax) >> 23) - (F8 ? 8 : 2), 0);
+      if constexpr (F8) {
+        // E4M3: the converter does not saturate (beyond 448 it returns NaN),
+        // so the clip bounds are narrowed to +-448 * 2^e, which clamps every
+        // value the way rounding with saturation would.
+        uint32_t wq[4];
+        if (__builtin_amdgcn_ballot_w64(sbyte == 0) == 0) {
+          const float scale = __uint_as_float((uint32_t)sbyte << 23);  // 2^e
+          const float sat = 448.0f * scale;                             // exact
+          const float u8 = fminf(u, sat);
+          const float l8 = fminf(fmaxf(l, -sat), u8);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v2i16 r = {0, 0};
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(acc[4 * q], l8, u8),
+                                                         __builtin_amdgcn_fmed3f(acc[4 * q + 1], l8, u8), scale, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(acc[4 * q + 2], l8, u8),
+                                                         __builtin_amdgcn_fmed3f(acc[4 * q + 3], l8, u8), scale, true);
+            wq[q] = __builtin_bit_cast(uint32_t, r);
+          }
+        } else {
+          const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-e, exact
+#define BATQ_V8(r) __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(acc[r], l, u) * inv, -448.0f, 448.0f)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v2i16 r = {0, 0};
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, BATQ_V8(4 * q), BATQ_V8(4 * q + 1), 1.0f, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, BATQ_V8(4 * q + 2), BATQ_V8(4 * q + 3), 1.0f, true);
+            wq[q] = __builtin_bit_cast(uint32_t, r);
+          }
+#undef BATQ_V8
+        }
+        // wq[q] holds channels 8q + 4h .. 8q + 4h + 3.  Half 0 keeps channels
+        // 0..15 (its q0, q1 and the partner's), half 1 channels 16..31.
+        const uint32_t s0 = h ? wq[0] : wq[2];
+        const uint32_t s1 = h ? wq[1] : wq[3];
+        const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+        const uint32_t p0 = h ? r0[0] : r0[1];
+        const uint32_t p1 = h ? r1[0] : r1[1];
+        const uint4 out = h ? make_uint4(p0, wq[2], p1, wq[3]) : make_uint4(wq[0], p0, wq[1], p1);
+        *reinterpret_cast<uint4*>(qs + row * T::kQRow + 32 * wave + 16 * h) = out;
+        if (h == 0) ss[row * 8 + wave] = (uint8_t)sbyte;
+      } else {
 
       // The converter divides by its scale operand, so 2^e goes in directly
       // (z / 2^e is exact).  2^-127 (scale byte 0, a block below 2^-125) is
@@ -310,18 +359,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const uint32_t out_hi = (first >> 16) | (second & 0xFFFF0000u);
       *reinterpret_cast<uint2*>(qs + row * T::kQRow + 16 * wave + 8 * h) = make_uint2(out_lo, out_hi);
       if (h == 0) ss[row * 8 + wave] = (uint8_t)sbyte;
+      }  // E2M1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
     block_barrier();                      // B_i
     if (wave == kStorerWave) {
+      // code bytes per row of the tile: 16 (E2M1) or 32 (E4M3) per block
+      constexpr int kChunks = F8 ? 16 : 8;  // 16-byte chunks per staged row
 #pragma unroll
-      for (int k = 0; k < kTT * 8 / 64; ++k) {
+      for (int k = 0; k < kTT * kChunks / 64; ++k) {
         const int id = lane + 64 * k;
-        const int row = id >> 3;
-        const int c = id & 7;
+        const int row = id / kChunks;
+        const int c = id % kChunks;
         const int64_t tok = tok0 + row;
-        if (tok < p.rows && c < nblk)
-          *reinterpret_cast<uint4*>(p.q + tok * qld + blk0 * 16 + 16 * c) =
+        if (tok < p.rows && c / (kChunks / 8) < nblk)
+          *reinterpret_cast<uint4*>(p.q + tok * qld + blk0 * (2 * kChunks) + 16 * c) =
               *reinterpret_cast<const uint4*>(qs + row * T::kQRow + 16 * c);
       }
       if (lane < kTT) {
@@ -354,10 +406,18 @@ hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t st
   if (gy > tiles) gy = tiles;
   if (gy > 65535) gy = 65535;
   dim3 grid((unsigned)gx, (unsigned)gy);
-  if (args.r_hi != nullptr && args.r_ld != 0)
-    hipLaunchKernelGGL(transform_quant_kernel<true>, grid, dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL(transform_quant_kernel<false>, grid, dim3(kThreads), 0, stream, args);
+  const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
+  if (args.fp8) {
+    if (per_row)
+      hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL((transform_quant_kernel<false, true>), grid, dim3(kThreads), 0, stream, args);
+  } else {
+    if (per_row)
+      hipLaunchKernelGGL((transform_quant_kernel<true, false>), grid, dim3(kThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL((transform_quant_kernel<false, false>), grid, dim3(kThreads), 0, stream, args);
+  }
   return hipGetLastError();
 }
 
