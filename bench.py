@@ -30,7 +30,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix, published
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix, published: the FP8 x FP4 MFMA's rate
 METRIC = "transform+MXFP4-quant GB/s (% HBM peak); MXFP4 GEMM TFLOPS (% MFMA peak)"
+METRIC_W4A8 = "transform+MXFP8-quant GB/s (% HBM peak); MXFP8 x MXFP4 GEMM TFLOPS (% MFMA peak)"
 CACHE_BYTES = 256 * 2 ** 20
 
 
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--no-clip", action="store_true", help="no block-wise clipping (activations and weights)")
     ap.add_argument("--gemm", choices=["packed", "unpacked"], default="packed",
                     help="weight operand layout of the GEMM (packed: lane-ordered, prepared offline)")
+    ap.add_argument("--act-format", choices=["mxfp4", "mxfp8"], default="mxfp4",
+                    help="activation format: mxfp4 (W4A4) or mxfp8 (W4A8, E4M3; packed GEMM only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (HBM counter calibration)")
@@ -78,7 +82,7 @@ def load_traffic(kernel_file: str, kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(wl, min_seconds: float):
+def cpu_baseline(wl, min_seconds: float, fmt: str = "e2m1"):
     """The oracle, as it stands, on the same workload: the whole step (every
     token row through the activation path, then the full GEMM against every
     prepared weight row), repeated until ``min_seconds`` have passed."""
@@ -90,9 +94,9 @@ def cpu_baseline(wl, min_seconds: float):
     reps, t_act, t_gemm = 0, 0.0, 0.0
     while reps == 0 or (t_act + t_gemm < min_seconds and reps < 8):
         t0 = time.perf_counter()
-        x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+        x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta, fmt=fmt)
         t1 = time.perf_counter()
-        ob.gemm(x.codes, x.scales, wprep.codes, wprep.scales)
+        ob.gemm(x.codes, x.scales, wprep.codes, wprep.scales, x_fmt=fmt)
         t2 = time.perf_counter()
         t_act += t1 - t0
         t_gemm += t2 - t1
@@ -139,6 +143,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    fp8 = args.act_format == "mxfp8"
+    if fp8 and args.gemm != "packed":
+        print("--act-format mxfp8 runs on the packed GEMM only", file=sys.stderr)
+        sys.exit(2)
     import torch
 
     import w4a4_bit_gemm_amd as w
@@ -173,7 +181,8 @@ def main():
     Wp0 = w.weight_pack(Wq0, Ws0) if packed else None  # offline
     torch.cuda.synchronize()
 
-    set_bytes = M * K * 2 + M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
+    xq_row = K if fp8 else K // 2  # activation code bytes per row
+    set_bytes = M * K * 2 + M * xq_row + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
     nsets = max(2, int(np.ceil(2.2 * CACHE_BYTES / set_bytes)))
     nsets = min(nsets, 16)
     sets = []
@@ -182,18 +191,20 @@ def main():
             X=X0.clone(),
             Wq=None if packed else Wq0.clone(), Ws=None if packed else Ws0.clone(),
             Wp=w.PackedWeight(Wp0.data.clone(), N, K) if packed else None,
-            Xq=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            Xq=torch.empty((M, xq_row), dtype=torch.uint8, device=dev),
             Xs=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
             Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     torch.cuda.synchronize()
 
     def act(i):
         s = sets[i % nsets]
-        w.act_transform_quant(s["X"], A, B, rh, rl, out=(s["Xq"], s["Xs"]))
+        (w.act_transform_quant_mxfp8 if fp8 else w.act_transform_quant)(s["X"], A, B, rh, rl, out=(s["Xq"], s["Xs"]))
 
     def gemm(i):
         s = sets[i % nsets]
-        if packed:
+        if fp8:
+            w.mxfp8_gemm_packed(s["Xq"], s["Xs"], s["Wp"], out=s["Y"])
+        elif packed:
             w.mxfp4_gemm_packed(s["Xq"], s["Xs"], s["Wp"], out=s["Y"])
         else:
             w.mxfp4_gemm(s["Xq"], s["Xs"], s["Wq"], s["Ws"], out=s["Y"])
@@ -232,17 +243,18 @@ def main():
     t_gemm = np.array([batch_seconds(gemm)])
 
     flops = 2.0 * M * N * K
-    act_bytes = M * K * 2 + M * K // 2 + M * K // 32  # algorithmic: read bf16, write codes + scales
-    gemm_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
+    act_bytes = M * K * 2 + M * xq_row + M * K // 32  # algorithmic: read bf16, write codes + scales
+    gemm_bytes = M * xq_row + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
+    mma_peak = FP8_PEAK_TFLOPS if fp8 else MXFP4_PEAK_TFLOPS
     act_gbs = act_bytes / t_act.mean() / 1e9
     gemm_tflops = flops / t_gemm.mean() / 1e12
     ai = flops / gemm_bytes
-    gemm_hbm_bound = ai < MXFP4_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    gemm_hbm_bound = ai < mma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if gemm_hbm_bound:
         gemm_roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm.mean() / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s"}
     else:
-        gemm_roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        gemm_roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": mma_peak, "unit": "TFLOP/s"}
     gemm_roof["frac"] = gemm_roof["achieved"] / gemm_roof["peak"]
     act_roof = {"bound": "hbm", "achieved": act_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": act_gbs / HBM_PEAK_GBS}
@@ -251,16 +263,17 @@ def main():
     gemm_src = "mxfp4_gemm_packed.hip" if packed else "mxfp4_gemm.hip"
     nst = K // 256
     gs = "true" if nst % 4 == 0 else "false"
-    gemm_kernel = (f"mxfp4_gemm_packed_kernel<{nst if nst in (1, 2, 4, 8, 16, 48) else 0},{gs}>" if packed
+    a8 = "true" if fp8 else "false"
+    gemm_kernel = (f"mxfp4_gemm_packed_kernel<{nst if nst in (1, 2, 4, 8, 16, 48) else 0},{gs},{a8}>" if packed
                    else "mxfp4_gemm_dma_kernel")
-    act_kernel = "transform_quant_kernel<false>"
+    act_kernel = f"transform_quant_kernel<false,{a8}>"
     act_roof["traffic"] = load_traffic("transform_quant.hip", act_kernel, wl.name)
     gemm_roof["traffic"] = load_traffic(gemm_src, gemm_kernel, wl.name)
     roof["traffic"] = gemm_roof["traffic"] if dominant_is_gemm else act_roof["traffic"]
     roof["kernel"] = gemm_kernel if dominant_is_gemm else act_kernel
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_W4A8 if fp8 else METRIC,
         "value": flops / (ms_per_step * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -270,30 +283,31 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": "mxfp8xmxfp4" if fp8 else "mxfp4",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), "
                         f"W {N}x{K} bf16 N(0,0.02) prepared offline ({args.gemm} MXFP4); "
+                        f"{'MXFP8 (E4M3) activations; ' if fp8 else ''}"
                         f"{'block-Hadamard (BRQ) factors' if args.factors == 'hadamard' else 'GPK'} a={wl.a} b={wl.b}"
                         f"{', no clipping' if args.no_clip else ''}; "
-                        f"step = act transform+clip+MXFP4 quant + MXFP4 GEMM (bf16 out)",
+                        f"step = act transform+clip+{args.act_format.upper()} quant + GEMM (bf16 out)",
             "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets, "gemm": args.gemm,
-            "factors": args.factors, "clip": not args.no_clip,
+            "factors": args.factors, "clip": not args.no_clip, "act_format": args.act_format,
         },
         "roofline": roof,
         "kernels": {
             "transform_quant": {"us": float(t_act.mean() * 1e6), "GB/s": act_gbs,
                                 "frac_hbm": act_gbs / HBM_PEAK_GBS, "algorithmic_bytes": act_bytes,
                                 "roofline": act_roof},
-            "mxfp4_gemm": {"kernel": gemm_kernel, "us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
-                           "frac_mfma": gemm_tflops / MXFP4_PEAK_TFLOPS, "flops": flops,
-                           "operand_output_bytes": gemm_bytes, "roofline": gemm_roof},
+            "gemm": {"kernel": gemm_kernel, "us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
+                     "frac_mfma": gemm_tflops / mma_peak, "flops": flops,
+                     "operand_output_bytes": gemm_bytes, "roofline": gemm_roof},
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds, "e4m3" if fp8 else "e2m1")
     print(json.dumps(out), flush=True)
 
 
