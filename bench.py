@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -58,10 +59,22 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest(name: str) -> str:
-    path = os.path.join(ROOT, "w4a4_bit_gemm_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_digest(name: str, text_of=None) -> str:
+    """sha256[:16] of a kernel source plus the shared header, with comments and
+    blank space removed: a comment edit keeps a counter summary valid, any code
+    change invalidates it."""
+    def read(rel):
+        if text_of is not None:
+            return text_of(rel)
+        with open(os.path.join(ROOT, "w4a4_bit_gemm_amd", "csrc", rel)) as f:
+            return f.read()
+
+    parts = []
+    for rel in (name, "common.h"):
+        t = re.sub(r"/\*.*?\*/", "", read(rel), flags=re.S)
+        t = re.sub(r"//[^\n]*", "", t)
+        parts.append("\n".join(ln.strip() for ln in t.splitlines() if ln.strip()))
+    return hashlib.sha256("\n\0\n".join(parts).encode()).hexdigest()[:16]
 
 
 def load_traffic(kernel_file: str, kernel: str, workload: str):

@@ -24,6 +24,13 @@
 // lane-local plus one cross-half exchange.  E2M1 rounding uses the hardware
 // converter v_cvt_scalef32_pk_fp4_f32 (round to nearest even, saturating,
 // sign-preserving) on z * 2^-e, which is exact.
+//
+// The same kernel also produces MXFP8 (E4M3) codes for the W4A8 setting
+// [nubint.ai review, Table 2]: e = floor(log2 max|z|) - 8 (the largest E4M3
+// exponent), one byte per element.  Its converter v_cvt_scalef32_pk_fp8_f32
+// rounds to nearest even with subnormals but does not saturate (it returns the
+// NaN code above 448), so z is clamped to +-448 * 2^e first, which leaves the
+// round-to-nearest decision unchanged.
 #include "common.h"
 
 namespace batq {
@@ -172,14 +179,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     rl_blk = p.r_lo[blk];
   }
 
-  // Loader: tile i (< ntile) -> its slot; one tile is kTT / 2 load instructions,
-  // instruction q covering rows 2q and 2q + 1.  Lane l fetches row
-  // 2q + l / 32, logical 16-byte chunk c = (l % 32) ^ (row % 16) (chunks past K
-  // read a valid column, unused).  The swizzle repeats every 8 instructions, so
-  // the lane's offset within the tile is precomputed for q = 0..7; a full tile
-  // then costs one 64-bit add per instruction.
   const bool loader = wave == kLoaderWave;
-  // Loader addressing: a buffer descriptor based at the tile's first row whose
+  // Loader: tile i (< ntile) -> its slot, kTT / 2 load instructions per tile.
+  // Addressing: a buffer descriptor based at the tile's first row whose
   // size ends at the last row of X (the hardware range check turns rows past
   // the end into zeros, which are never stored), plus per-lane byte offsets
   // within the tile.  Instruction q covers rows 2q and 2q + 1: lane l fetches
