@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix, published
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix, published: the FP8 x FP4 MFMA's rate
 METRIC = "transform+MXFP4-quant GB/s (% HBM peak); MXFP4 GEMM TFLOPS (% MFMA peak)"
-METRIC_W4A8 = "transform+MXFP8-quant GB/s (% HBM peak); MXFP8 x MXFP4 GEMM TFLOPS (% MFMA peak)"
+METRIC_W4A8 = "transform+MXFP8-quant GB/s (% HBM peak); MXFP8 x MXFP4 GEMM TFLOP/s (% MFMA peak)"
+METRIC_DECODE = "fused decode step (transform+MXFP4 quant in the GEMM prologue) GB/s (% HBM peak)"
 CACHE_BYTES = 256 * 2 ** 20
 
 
@@ -51,6 +52,10 @@ def parse():
                     help="weight operand layout of the GEMM (packed: lane-ordered, prepared offline)")
     ap.add_argument("--act-format", choices=["mxfp4", "mxfp8"], default="mxfp4",
                     help="activation format: mxfp4 (W4A4) or mxfp8 (W4A8, E4M3; packed GEMM only)")
+    ap.add_argument("--decode", action="store_true",
+                    help="fused decode step (w4a4_decode: activation path inside the GEMM), M <= 32 (config 4)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: replay the steps from a captured HIP graph (no host launch overhead)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (HBM counter calibration)")
@@ -59,18 +64,21 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest(name: str, text_of=None) -> str:
-    """sha256[:16] of a kernel source plus the shared header, with comments and
-    blank space removed: a comment edit keeps a counter summary valid, any code
-    change invalidates it."""
+def kernel_source_digest(name: str, text_of=None, headers=None) -> str:
+    """sha256[:16] of a kernel source plus the shared headers (every .h in
+    csrc/), with comments and blank space removed: a comment edit keeps a
+    counter summary valid, any code change invalidates it."""
     def read(rel):
         if text_of is not None:
             return text_of(rel)
         with open(os.path.join(ROOT, "w4a4_bit_gemm_amd", "csrc", rel)) as f:
             return f.read()
 
+    if headers is None:
+        headers = sorted(os.path.basename(h) for h in
+                         __import__("glob").glob(os.path.join(ROOT, "w4a4_bit_gemm_amd", "csrc", "*.h")))
     parts = []
-    for rel in (name, "common.h"):
+    for rel in [name] + list(headers):
         t = re.sub(r"/\*.*?\*/", "", read(rel), flags=re.S)
         t = re.sub(r"//[^\n]*", "", t)
         parts.append("\n".join(ln.strip() for ln in t.splitlines() if ln.strip()))
@@ -128,7 +136,117 @@ def cpu_baseline(wl, min_seconds: float, fmt: str = "e2m1"):
                    f"and untimed; BLAS threads {blas_threads}, host cores visible "
                    f"{len(os.sched_getaffinity(0))}"),
         "seconds_measured": t_act + t_gemm,
+        "steps_per_second": reps / (t_act + t_gemm),
     }
+
+
+def run_decode(args, torch, w, wl, dev):
+    """The fused decode step: one w4a4_decode call (the activation transform,
+    clip and MXFP4 quantisation run inside the GEMM kernel; a second small
+    launch sums its K splits).  Bound: HBM (the packed weights are read once
+    per step).  Buffers rotate over enough sets that every step reads its
+    weights from HBM."""
+    M, K, N = wl.M, wl.K, wl.N
+    if M > w.DECODE_MAX_M:
+        print(f"--decode needs M <= {w.DECODE_MAX_M} (config 4); config {args.config} has M = {M}", file=sys.stderr)
+        sys.exit(2)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    if args.factors == "hadamard":
+        wl.A, wl.B = gen.hadamard_factors(K, wl.a)
+    if args.no_clip:
+        wl.alpha = wl.beta = wl.walpha = wl.wbeta = None
+    A, B = f32(wl.A), f32(wl.B)
+    rh = None if args.no_clip else f32(w.clip_ratios(wl.alpha))
+    rl = None if args.no_clip else f32(w.clip_ratios(wl.beta))
+    Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)  # offline
+    Wp0 = w.weight_pack(Wq0, Ws0)
+    X0 = bf16(wl.X_bits)
+    ws = w.decode_workspace(M, N, K, dev)
+    wp_bytes = Wp0.data.numel()
+    set_bytes = M * K * 2 + wp_bytes + M * N * 2
+    nsets = min(64, max(2, int(np.ceil(2.2 * CACHE_BYTES / set_bytes))))
+    sets = [dict(X=X0.clone(), Wp=w.PackedWeight(Wp0.data.clone(), N, K),
+                 Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        st = sets[i % nsets]
+        w.w4a4_decode(st["X"], A, B, rh, rl, st["Wp"], ws, out=st["Y"])
+
+    steps = args.steps
+    if args.graph:
+        # one captured graph holds one step per buffer set; the timed steps are
+        # a whole number of replays
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            for i in range(nsets):
+                step(i)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(nsets):
+                    step(i)
+        torch.cuda.synchronize()
+        reps = -(-steps // nsets)
+        steps = reps * nsets
+        run = lambda: [g.replay() for _ in range(reps)]
+        for _ in range(max(1, -(-args.warmup // nsets))):
+            g.replay()
+    else:
+        run = lambda: [step(i) for i in range(steps)]
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = e0.elapsed_time(e1) * 1e-3 / steps  # GPU time per step, events on the launch stream
+    alg_bytes = M * K * 2 + wp_bytes + M * N * 2  # X read, packed weights read, Y written
+    gbs = alg_bytes / t_step / 1e9
+    out = {
+        "metric": METRIC_DECODE,
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), W {N}x{K} bf16 "
+                        f"N(0,0.02) prepared and packed offline; step = one fused decode launch pair "
+                        f"({'graph replay' if args.graph else 'eager launches'})",
+            "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets, "graph": args.graph,
+            "factors": args.factors, "clip": not args.no_clip,
+        },
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_partial_kernel + decode_reduce_kernel (one step)"},
+        "kernels": {"decode_step": {"us": t_step * 1e6, "GB/s": gbs, "algorithmic_bytes": alg_bytes,
+                                    "TFLOP/s": 2.0 * M * N * K / t_step / 1e12}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, args.cpu_min_seconds)
+        cb["value"] = alg_bytes * cb["steps_per_second"] / 1e9
+        cb["unit"] = "GB/s"
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
 
 
 def calibrate_copy(torch, dev, steps):
@@ -173,6 +291,9 @@ def main():
         return
     wl = gen.make_workload(args.config, a=args.a)
     M, K, N = wl.M, wl.K, wl.N
+    if args.decode:
+        run_decode(args, torch, w, wl, dev)
+        return
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -197,7 +318,7 @@ def main():
     xq_row = K if fp8 else K // 2  # activation code bytes per row
     set_bytes = M * K * 2 + M * xq_row + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
     nsets = max(2, int(np.ceil(2.2 * CACHE_BYTES / set_bytes)))
-    nsets = min(nsets, 16)
+    nsets = min(nsets, 64)
     sets = []
     for _ in range(nsets):
         sets.append(dict(

@@ -198,6 +198,43 @@ batq_status batq_act_transform_quant_mxfp8(const void* X_bf16, int64_t M, int64_
 batq_status batq_mxfp8_gemm_packed(const uint8_t* Xq8, const uint8_t* Xs, const uint8_t* Wp, int64_t M,
                                    int64_t N, int64_t K, void* Y, batq_out_dtype out, hipStream_t stream);
 
+/* ------------------------------------------------ fused decode step
+ * For decode-sized batches the online transform and quantisation run inside
+ * the GEMM's prologue instead of as a separate launch [en.papernotes.org, Key
+ * Designs §1-§4 and A Worked Example: transform, clip, quantise, multiply;
+ * the pages report the online transform's cost as the decode overhead].
+ */
+#define BATQ_DECODE_MAX_M 32
+
+/* Workspace bytes batq_w4a4_decode needs for (M, N, K): fp32 partial tiles,
+ * one per 256-column chunk, K split and token.  -1 for M outside [0, 32],
+ * N < 0 or K not a positive multiple of 256. */
+int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Y[M][N] = deq(Q(X P)) deq(Wp)^T with the activation path fused into the
+ * GEMM: the block transform, clip and MXFP4 quantisation of X (bit-identical
+ * to batq_act_transform_quant) feed the block-scaled MFMA against weights
+ * packed by batq_weight_pack inside one kernel, split over 256-column chunks
+ * and ranges of K; a second, small launch sums the K ranges' fp32 partials in
+ * a fixed order, so results are deterministic and within the fp32
+ * accumulation bound of the unsplit product.
+ * X_bf16: [M][ldx] bf16, 1 <= M <= 32 (M == 0 or N == 0 is a no-op), K a
+ * multiple of 256, ldx >= K and a multiple of 8, X 16-byte aligned.  A, B,
+ * r_hi, r_lo: as for batq_act_transform_quant (ratios may both be NULL: no
+ * clipping).  Wp: packed weights for (N, K), 16-byte aligned.  Y: [M][N] bf16
+ * or float, 4-byte aligned.  Xq [M][K/2] (8-byte aligned) and Xs [M][K/32]:
+ * optional, both NULL or both set; when set they also receive the quantised
+ * activations.  workspace: device memory of at least
+ * batq_decode_workspace_bytes(M, N, K) bytes, 256-byte aligned, owned by the
+ * caller, any contents (the call overwrites what it reads).  Calls that share
+ * a workspace must not overlap (use one stream).
+ * Errors: SHAPE (also a workspace that is too small), NULL, ALIGN,
+ * UNSUPPORTED (factor size or output type), HIP. */
+batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
+                             const float* A, const float* B, const float* r_hi, const float* r_lo,
+                             const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq, uint8_t* Xs,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -106,3 +106,20 @@ def w4a8_gemm_bound(xc, xs, wc, ws) -> np.ndarray:
     Xd = ob.dequantize(xc, xs, "e4m3")
     Wd = ob.dequantize(wc, ws)
     return gemm_bound(np.abs(Xd) @ np.abs(Wd).T, Xd.shape[1]) + f8f4_window_bound(Xd, Wd)
+
+
+def free_decision_bound(xdec: ob.Decisions, wdec: ob.Decisions) -> np.ndarray:
+    """Largest change of Y = deq(X) deq(W)^T that the oracle's free decisions
+    allow, per output [M, N]: a free code may land on an adjacent E2M1 value (a
+    step of at most 2 at scale 2^e), a free block scale may move by one, which
+    changes each element of the block by at most 18 2^e (6 2^(e+1) + 6 2^e)."""
+    def delta(dec):
+        e = np.ldexp(1.0, dec.scales.astype(np.int64) - 127)
+        step = np.repeat(2.0 * e, ob.BLOCK, axis=1)
+        blk = np.repeat(dec.block_free, ob.BLOCK, axis=1)
+        d = np.where(dec.elem_free, step, 0.0)
+        return np.where(blk, np.repeat(18.0 * e, ob.BLOCK, axis=1), d)
+    ax = np.abs(ob.dequantize(xdec.codes, xdec.scales))
+    aw = np.abs(ob.dequantize(wdec.codes, wdec.scales))
+    dx, dw = delta(xdec), delta(wdec)
+    return ax @ dw.T + dx @ aw.T + dx @ dw.T

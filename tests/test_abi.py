@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ("batq_act_transform_quant", "batq_weight_prep", "batq_mxfp4_gemm", "batq_gpk_invert",
               "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
               "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
-              "batq_mxfp8_gemm_packed"):
+              "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode"):
         assert n in names
 
 
@@ -124,6 +124,47 @@ def test_packed_gemm_argument_checks(lib, name):
     assert f(FAKE, FAKE, FAKE, 4, 4, 256, FAKE + 2, 0, None) == ALIGN
     assert f(FAKE, FAKE, FAKE, 0, 4, 256, FAKE, 0, None) == OK
     assert f(FAKE, FAKE, FAKE, 4, 0, 256, FAKE, 1, None) == OK
+
+
+def test_decode_workspace_bytes(lib):
+    f = lib.batq_decode_workspace_bytes
+    assert f(16, 4096, 4096) == 16 * 16 * 16 * 256 * 4      # one stage per K split
+    assert f(1, 300, 512) == 2 * 2 * 1 * 256 * 4
+    assert f(4, 12288, 4096) == 48 * 8 * 4 * 256 * 4        # two stages per split
+    assert f(8, 12288, 12288) == 48 * 12 * 8 * 256 * 4      # four stages per split
+    assert f(0, 256, 256) == 0
+    assert f(33, 256, 256) == -1 and f(-1, 256, 256) == -1
+    assert f(4, 256, 100) == -1 and f(4, 256, 0) == -1 and f(4, -1, 256) == -1
+
+
+def _dec(lib, x=FAKE, M=4, K=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0, wp=FAKE, N=256, y=FAKE, out=0,
+         xq=0, xs=0, ws=FAKE, wsb=1 << 30):
+    return lib.batq_w4a4_decode(x, M, K, ld, a, b, A, B, rh, rl, wp, N, y, out, xq, xs, ws, wsb, None)
+
+
+def test_decode_argument_checks(lib):
+    assert _dec(lib, M=33) == SHAPE
+    assert _dec(lib, M=-1) == SHAPE
+    assert _dec(lib, K=224, ld=256) == SHAPE
+    assert _dec(lib, K=0, ld=0) == SHAPE
+    assert _dec(lib, ld=128) == SHAPE
+    assert _dec(lib, a=8, b=8) == SHAPE
+    assert _dec(lib, wsb=lib.batq_decode_workspace_bytes(4, 256, 256) - 1) == SHAPE
+    assert _dec(lib, a=-1, b=-32) == UNSUP
+    assert _dec(lib, out=5) == UNSUP
+    for kw in ("x", "A", "B", "wp", "y", "ws"):
+        assert _dec(lib, **{kw: 0}) == NULL, kw
+    assert _dec(lib, rh=FAKE) == NULL
+    assert _dec(lib, xq=FAKE) == NULL
+    assert _dec(lib, x=FAKE + 2) == ALIGN
+    assert _dec(lib, ld=260, K=256) == ALIGN
+    assert _dec(lib, wp=FAKE + 8) == ALIGN
+    assert _dec(lib, y=FAKE + 2) == ALIGN
+    assert _dec(lib, ws=FAKE + 16) == ALIGN
+    assert _dec(lib, xq=FAKE + 4, xs=FAKE) == ALIGN
+    # empty batch or no columns: no-ops that return before touching the GPU
+    assert _dec(lib, M=0) == OK
+    assert _dec(lib, N=0) == OK
 
 
 def test_clip_ratios_match_oracle():

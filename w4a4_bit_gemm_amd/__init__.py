@@ -21,4 +21,8 @@ from .binding import (  # noqa: F401
     weight_packed_bytes,
     prepare_weight,
     weight_prep,
+    DECODE_MAX_M,
+    decode_workspace,
+    decode_workspace_bytes,
+    w4a4_decode,
 )

@@ -67,6 +67,11 @@ def _load():
                                                     P, P, P]
     lib.batq_mxfp8_gemm_packed.restype = ctypes.c_int
     lib.batq_mxfp8_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    lib.batq_decode_workspace_bytes.restype = I64
+    lib.batq_decode_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.batq_w4a4_decode.restype = ctypes.c_int
+    lib.batq_w4a4_decode.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, P, ctypes.c_int, P, P, P, I64,
+                                     P]
     _lib = lib
     return lib
 
@@ -315,5 +320,62 @@ def mxfp8_gemm_packed(Xq8, Xs, Wp: PackedWeight, out_dtype=None, out=None):
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
     st = _load().batq_mxfp8_gemm_packed(_ptr(Xq8), _ptr(Xs), _ptr(Wp.data), M, N, K, _ptr(out), code,
                                         _stream_ptr(torch, Xq8.device))
+    _check(st)
+    return out
+
+
+DECODE_MAX_M = 32
+
+
+def decode_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Bytes of workspace :func:`w4a4_decode` needs (-1 for unsupported shapes)."""
+    return int(_load().batq_decode_workspace_bytes(M, N, K))
+
+
+def decode_workspace(M: int, N: int, K: int, device):
+    """A workspace for :func:`w4a4_decode` (256-byte aligned as allocated by the
+    PyTorch caching allocator; one per stream)."""
+    torch = _torch()
+    n = decode_workspace_bytes(M, N, K)
+    if n < 0:
+        raise ValueError(f"unsupported decode shape M={M} N={N} K={K}")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None, out=None,
+                quantized_out: Optional[tuple] = None):
+    """Fused decode step: transform + clip + MXFP4 quantisation of X (M <= 32
+    tokens) inside the GEMM against packed weights, one launch.
+
+    X: [M, K] bf16; A, B, r_hi, r_lo as for :func:`act_transform_quant`;
+    workspace: from :func:`decode_workspace` (one per stream).
+    quantized_out: optional (Xq [M, K/2], Xs [M, K/32]) uint8 tensors that also
+    receive the quantised activations.  Returns Y [M, N].
+    """
+    torch = _torch()
+    _req(X, torch.bfloat16, "X")
+    _req(A, torch.float32, "A")
+    _req(B, torch.float32, "B")
+    if (r_hi is None) != (r_lo is None):
+        raise ValueError("r_hi and r_lo must both be given or both be None")
+    if r_hi is not None:
+        _req(r_hi, torch.float32, "r_hi")
+        _req(r_lo, torch.float32, "r_lo")
+    _req(workspace, torch.uint8, "workspace")
+    M, K = X.shape
+    if K != Wp.K:
+        raise ValueError("X and the packed weight disagree on K")
+    N = Wp.N
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    else:
+        _req(out, out_dtype, "out")
+    Xq, Xs = quantized_out if quantized_out is not None else (None, None)
+    code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    st = _load().batq_w4a4_decode(_ptr(X), M, K, X.stride(0), A.shape[0], B.shape[-1], _ptr(A), _ptr(B),
+                                  _ptr(r_hi), _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
+                                  _ptr(workspace), workspace.numel(), _stream_ptr(torch, X.device))
     _check(st)
     return out

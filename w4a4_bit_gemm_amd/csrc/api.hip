@@ -240,4 +240,48 @@ batq_status batq_mxfp8_gemm_packed(const uint8_t* Xq8, const uint8_t* Xs, const 
   return batq::launch_mxfp4_gemm_packed(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 
+
+int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || K <= 0 || K % 256 != 0) return -1;
+  return batq::decode_workspace_bytes(M, N, K);
+}
+
+batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
+                             const float* A, const float* B, const float* r_hi, const float* r_lo, const uint8_t* Wp,
+                             int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq, uint8_t* Xs, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || K <= 0 || K % 256 != 0 || ldx < K) return BATQ_ERR_SHAPE;
+  if ((int64_t)a * (int64_t)b != 32) return BATQ_ERR_SHAPE;
+  if (!is_pow2_factor(a)) return BATQ_ERR_UNSUPPORTED;
+  if (out != BATQ_OUT_BF16 && out != BATQ_OUT_F32) return BATQ_ERR_UNSUPPORTED;
+  if (X_bf16 == nullptr || A == nullptr || B == nullptr || Wp == nullptr || Y == nullptr || workspace == nullptr)
+    return BATQ_ERR_NULL;
+  if ((r_hi == nullptr) != (r_lo == nullptr) || (Xq == nullptr) != (Xs == nullptr)) return BATQ_ERR_NULL;
+  if (!aligned(X_bf16, 16) || ldx % 8 != 0 || !aligned(Wp, 16) || !aligned(Y, 4) || !aligned(workspace, 256))
+    return BATQ_ERR_ALIGN;
+  if (!aligned(A, 4) || !aligned(B, 4) || (r_hi && (!aligned(r_hi, 4) || !aligned(r_lo, 4))) ||
+      (Xq && !aligned(Xq, 8)))
+    return BATQ_ERR_ALIGN;
+  if (workspace_bytes < batq::decode_workspace_bytes(M, N, K)) return BATQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return BATQ_OK;
+  batq::DecodeArgs args;
+  args.x = static_cast<const uint16_t*>(X_bf16);
+  args.ldx = ldx;
+  args.M = M;
+  args.K = K;
+  args.N = N;
+  args.a_log2 = log2_exact(a);
+  args.A = A;
+  args.B = B;
+  args.r_hi = r_hi;
+  args.r_lo = r_lo;
+  args.wp = Wp;
+  args.y = Y;
+  args.out_f32 = out == BATQ_OUT_F32;
+  args.xq = Xq;
+  args.xs = Xs;
+  args.part = static_cast<float*>(workspace);
+  return batq::launch_decode_fused(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
+}
+
 }  // extern "C"

@@ -64,4 +64,25 @@ hipError_t launch_weight_pack(const uint8_t* wq, const uint8_t* ws, int64_t N, i
                               hipStream_t stream);
 // Same GemmArgs; wq points at the packed buffer and ws is unused.
 hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream);
+// Fused decode step (decode_fused.hip): transform + clip + MXFP4 quantisation
+// of M <= 32 tokens inside the GEMM on packed weights, split over
+// (256-column chunk, K split), then a split-order reduction launch.
+struct DecodeArgs {
+  const uint16_t* x;    // [M][ldx] bf16
+  int64_t ldx;
+  int64_t M, K, N;
+  int a_log2;
+  const float* A;       // [a][a]
+  const float* B;       // [K/32][b][b]
+  const float* r_hi;    // [K/32] or nullptr (no clipping)
+  const float* r_lo;
+  const uint8_t* wp;    // packed weights
+  void* y;              // [M][N]
+  int out_f32;
+  uint8_t* xq;          // optional [M][K/2] codes and [M][K/32] scales, or nullptr
+  uint8_t* xs;
+  float* part;          // workspace: fp32 partial tiles [N/256][splits][M][256]
+};
+int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_decode_fused(const DecodeArgs& args, hipStream_t stream);
 }  // namespace batq

@@ -31,7 +31,7 @@
 // rounds to nearest even with subnormals but does not saturate (it returns the
 // NaN code above 448), so z is clamped to +-448 * 2^e first, which leaves the
 // round-to-nearest decision unchanged.
-#include "common.h"
+#include "block_quant.h"
 
 namespace batq {
 
@@ -43,20 +43,6 @@ constexpr int kStorerWave = kBlocksPerWG - 2;  // also writes the staged codes a
 constexpr int kThreads = 64 * kBlocksPerWG;
 constexpr int kTT = 32;                        // tokens per tile (one MFMA group)
 constexpr int kRing = 4;                       // LDS tile slots; kRing - 1 tiles in flight
-
-// Exact product pa * pb split into three bf16 parts, hi + mid + lo, whose sum
-// differs from the product by at most ~2^-27 of it.
-__device__ __forceinline__ void split3(float pa, float pb, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  float r0 = pa * pb;
-  float e0 = __builtin_fmaf(pa, pb, -r0);  // exact rounding error of the product
-  hi = f32_to_bf16_rne(r0);
-  float rem = (r0 - bf16_to_f32(hi)) + e0;  // r0 - hi is exact
-  mid = f32_to_bf16_rne(rem);
-  float rem2 = rem - bf16_to_f32(mid);     // exact
-  lo = f32_to_bf16_rne(rem2);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -115,8 +101,6 @@ struct TQSmem {
   static constexpr int kQRow = F8 ? 272 : 144;
 };
 
-typedef short v2i16 __attribute__((ext_vector_type(2)));
-
 // PER_ROW: one ratio pair per (row, block), read per tile (the weight side);
 // otherwise one pair per block, read once (activations), which keeps every
 // memory wait out of the activations' tile loop.  F8: MXFP8 (E4M3) codes, one
@@ -146,30 +130,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int j = lane & 31;  // output channel (A-operand row) / token slot (B column)
   const int h = lane >> 5;  // which 8-channel half of each 16-channel k step
 
-  // P_i^T as MFMA A operand: lane holds P_i[16 ks + 8 h + t][j], t = 0..7, as
-  // an exact three-way bf16 split.
-  const int la = p.a_log2;
-  const int a = 1 << la;
-  const int amask = a - 1;
-  const int bdim = 32 >> la;
-  uint4 phi[2], pmid[2], plo[2];
-  {
-    const float* __restrict__ Bi = p.B + (blk_ok ? blk : 0) * bdim * bdim;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint32_t hw[8], mw[8], lw[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int k = 16 * ks + 8 * h + t;
-        const float bv = Bi[(k >> la) * bdim + (j >> la)];
-        const float av = p.A[(k & amask) * a + (j & amask)];
-        split3(bv, av, hw[t], mw[t], lw[t]);
-      }
-      phi[ks] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
-      pmid[ks] = make_uint4(mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16);
-      plo[ks] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
-    }
-  }
+  // P_i^T as MFMA A operand, exact three-way bf16 split.
+  const PSplit ps = build_p_split(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h);
   // Ratios shared by every token (activations) are read once here.
   const bool clip = p.r_hi != nullptr;
   const bool per_row = PER_ROW && clip;
@@ -239,30 +201,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const uint8_t* xr = xt + row * T::kXRow;
       uint4 x0, x1;
       lds_read2_b128(xr + 16 * ((4 * wave + h) ^ (row & 15)), xr + 16 * ((4 * wave + 2 + h) ^ (row & 15)), x0, x1);
-      f32x16 acc = {};
-      const bf16x8 bx0 = as_bf16x8(x0), bx1 = as_bf16x8(x1);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(plo[0]), bx0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(plo[1]), bx1, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pmid[0]), bx0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pmid[1]), bx1, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(phi[0]), bx0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(phi[1]), bx1, acc, 0, 0, 0);
+      const f32x16 acc = transform_block(ps, x0, x1);
       // acc[r] = y[token tok0 + row][channel 8 (r/4) + 4 h + r%4 of block blk]
-
-      float mx = acc[0], mn = acc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        mx = fmaxf(mx, acc[r]);
-        mn = fminf(mn, acc[r]);
-      }
-      {
-        // lanes l and l ^ 32 hold the two halves of a token's 32 channels
-        const auto smx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        const auto smn = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-        mx = fmaxf(__uint_as_float(smx[0]), __uint_as_float(smx[1]));
-        mn = fminf(__uint_as_float(smn[0]), __uint_as_float(smn[1]));
-      }
-
       float rh = rh_blk, rl = rl_blk;
       if (per_row) {
         int64_t tok = tok0 + row;
@@ -271,97 +211,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         rh = p.r_hi[ri];
         rl = p.r_lo[ri];
       }
-      const float u = __fmul_rn(rh, mx);
-      const float l = fminf(__fmul_rn(rl, mn), u);  // l > u clamps everything to u
-      const float zmax = __builtin_amdgcn_fmed3f(mx, l, u);
-      const float zmin = __builtin_amdgcn_fmed3f(mn, l, u);
-      const float amax = fmaxf(fabsf(zmax), fabsf(zmin));
-      // scale byte = e + 127 = max(biased exponent of amax - emax, 0), emax = 2
-      // for E2M1 and 8 for E4M3
-      const int sbyte = max((int)(__float_as_uint(amax) >> 23) - (F8 ? 8 : 2), 0);
+      int sbyte;
       if constexpr (F8) {
-        // E4M3: the converter does not saturate (beyond 448 it returns NaN),
-        // so the clip bounds are narrowed to +-448 * 2^e, which clamps every
-        // value the way rounding with saturation would.
-        uint32_t wq[4];
-        if (__builtin_amdgcn_ballot_w64(sbyte == 0) == 0) {
-          const float scale = __uint_as_float((uint32_t)sbyte << 23);  // 2^e
-          const float sat = 448.0f * scale;                             // exact
-          const float u8 = fminf(u, sat);
-          const float l8 = fminf(fmaxf(l, -sat), u8);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v2i16 r = {0, 0};
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(acc[4 * q], l8, u8),
-                                                         __builtin_amdgcn_fmed3f(acc[4 * q + 1], l8, u8), scale, false);
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(acc[4 * q + 2], l8, u8),
-                                                         __builtin_amdgcn_fmed3f(acc[4 * q + 3], l8, u8), scale, true);
-            wq[q] = __builtin_bit_cast(uint32_t, r);
-          }
-        } else {
-          const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-e, exact
-#define BATQ_V8(r) __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(acc[r], l, u) * inv, -448.0f, 448.0f)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v2i16 r = {0, 0};
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, BATQ_V8(4 * q), BATQ_V8(4 * q + 1), 1.0f, false);
-            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, BATQ_V8(4 * q + 2), BATQ_V8(4 * q + 3), 1.0f, true);
-            wq[q] = __builtin_bit_cast(uint32_t, r);
-          }
-#undef BATQ_V8
-        }
-        // wq[q] holds channels 8q + 4h .. 8q + 4h + 3.  Half 0 keeps channels
-        // 0..15 (its q0, q1 and the partner's), half 1 channels 16..31.
-        const uint32_t s0 = h ? wq[0] : wq[2];
-        const uint32_t s1 = h ? wq[1] : wq[3];
-        const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
-        const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
-        const uint32_t p0 = h ? r0[0] : r0[1];
-        const uint32_t p1 = h ? r1[0] : r1[1];
-        const uint4 out = h ? make_uint4(p0, wq[2], p1, wq[3]) : make_uint4(wq[0], p0, wq[1], p1);
-        *reinterpret_cast<uint4*>(qs + row * T::kQRow + 32 * wave + 16 * h) = out;
-        if (h == 0) ss[row * 8 + wave] = (uint8_t)sbyte;
+        *reinterpret_cast<uint4*>(qs + row * T::kQRow + 32 * wave + 16 * h) = quant_block_e4m3(acc, rh, rl, h, sbyte);
       } else {
-
-      // The converter divides by its scale operand, so 2^e goes in directly
-      // (z / 2^e is exact).  2^-127 (scale byte 0, a block below 2^-125) is
-      // not a normal float: such waves take the explicit multiply by 2^-e.
-      uint32_t wA = 0, wB = 0;
-#define BATQ_CVT(word, r, sel, M, S)                                                  \
-  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(                                    \
-      word, __builtin_amdgcn_fmed3f(acc[r], l, u) M, __builtin_amdgcn_fmed3f(acc[r + 1], l, u) M, S, sel)
-#define BATQ_CVT_ALL(M, S)                                                            \
-  BATQ_CVT(wA, 0, 0, M, S);                                                           \
-  BATQ_CVT(wA, 2, 1, M, S);                                                           \
-  BATQ_CVT(wA, 4, 2, M, S);                                                           \
-  BATQ_CVT(wA, 6, 3, M, S);                                                           \
-  BATQ_CVT(wB, 8, 0, M, S);                                                           \
-  BATQ_CVT(wB, 10, 1, M, S);                                                          \
-  BATQ_CVT(wB, 12, 2, M, S);                                                          \
-  BATQ_CVT(wB, 14, 3, M, S);
-      if (__builtin_amdgcn_ballot_w64(sbyte == 0) == 0) {
-        const float scale = __uint_as_float((uint32_t)sbyte << 23);  // 2^e
-        BATQ_CVT_ALL(, scale)
-      } else {
-        const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-e, exact
-        BATQ_CVT_ALL(*inv, 1.0f)
+        *reinterpret_cast<uint2*>(qs + row * T::kQRow + 16 * wave + 8 * h) = quant_block_e2m1(acc, rh, rl, h, sbyte);
       }
-#undef BATQ_CVT_ALL
-#undef BATQ_CVT
-      // Lane half h holds code bytes {4q + 2h, 4q + 2h + 1}, q = 0..3, with
-      // q = 0,1 in wA and q = 2,3 in wB.  Swap so that half 0 holds bytes 0..7
-      // and half 1 bytes 8..15 of the token's 16-byte code segment.
-      const uint32_t send = h ? wA : wB;
-      const auto sw = __builtin_amdgcn_permlane32_swap(send, send, false, false);
-      const uint32_t recv = h ? sw[0] : sw[1];  // the partner lane's word
-      const uint32_t keep = h ? wB : wA;
-      const uint32_t first = h ? recv : keep;
-      const uint32_t second = h ? keep : recv;
-      const uint32_t out_lo = (first & 0xFFFFu) | (second << 16);
-      const uint32_t out_hi = (first >> 16) | (second & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(qs + row * T::kQRow + 16 * wave + 8 * h) = make_uint2(out_lo, out_hi);
       if (h == 0) ss[row * 8 + wave] = (uint8_t)sbyte;
-      }  // E2M1
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
     block_barrier();                      // B_i
