@@ -76,7 +76,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Persistent workgroup: one column of 8 blocks (256 channels) and the token
-// tiles ty = blockIdx.y, blockIdx.y + gridDim.y, ... (32 tokens each), with
+// tiles ty = y, y + gy, ... (32 tokens each), with
 // two workgroups resident per CU.  Every wave w computes block blk0 + w: it
 // builds its P_i split once, then per tile runs the MFMA transform, clip,
 // scale and E2M1 codes into LDS staging buffers.  Two waves have a second
@@ -107,7 +107,7 @@ struct TQSmem {
 // byte per element (the W4A8 setting); otherwise MXFP4 (E2M1), two per byte.
 template <bool PER_ROW, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
-    TransformQuantArgs p) {
+    TransformQuantArgs p, int64_t gy) {
   using T = TQSmem<F8>;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kRing * T::kX];
   __shared__ __attribute__((aligned(16))) uint8_t qs[kTT * T::kQRow];
@@ -117,10 +117,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t nb = p.K >> 5;
-  const int64_t blk0 = (int64_t)blockIdx.x * kBlocksPerWG;
+  // Workgroup id = x gy + y: with gy a multiple of 8, every column group x of
+  // tile row y lands on the same XCD (ids go to the XCDs in turn), so the
+  // 8-byte scale pieces of a row's 128-byte scale line merge in one L2.
+  const int64_t blk0 = ((int64_t)blockIdx.x / gy) * kBlocksPerWG;
   const int64_t tiles = (p.rows + kTT - 1) / kTT;
-  const int64_t ty0 = blockIdx.y;
-  const int64_t tstep = gridDim.y;
+  const int64_t ty0 = (int64_t)blockIdx.x % gy;
+  const int64_t tstep = gy;
   const int64_t ntile = ty0 < tiles ? (tiles - ty0 + tstep - 1) / tstep : 0;  // uniform per workgroup
   const int64_t nblk = (nb - blk0) < kBlocksPerWG ? (nb - blk0) : kBlocksPerWG;  // valid blocks here
 
@@ -260,21 +263,21 @@ hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t st
   // resident round and let each workgroup walk its column's tiles.
   const int64_t target = 512;
   int64_t gy = target / gx;
+  if (gy >= 8) gy -= gy % 8;  // see the workgroup order in the kernel
   if (gy < 1) gy = 1;
   if (gy > tiles) gy = tiles;
-  if (gy > 65535) gy = 65535;
-  dim3 grid((unsigned)gx, (unsigned)gy);
+  const dim3 grid((unsigned)(gx * gy));
   const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
   if (args.fp8) {
     if (per_row)
-      hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args, gy);
     else
-      hipLaunchKernelGGL((transform_quant_kernel<false, true>), grid, dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL((transform_quant_kernel<false, true>), grid, dim3(kThreads), 0, stream, args, gy);
   } else {
     if (per_row)
-      hipLaunchKernelGGL((transform_quant_kernel<true, false>), grid, dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL((transform_quant_kernel<true, false>), grid, dim3(kThreads), 0, stream, args, gy);
     else
-      hipLaunchKernelGGL((transform_quant_kernel<false, false>), grid, dim3(kThreads), 0, stream, args);
+      hipLaunchKernelGGL((transform_quant_kernel<false, false>), grid, dim3(kThreads), 0, stream, args, gy);
   }
   return hipGetLastError();
 }
