@@ -34,6 +34,7 @@ MXFP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix, published
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix, published: the FP8 x FP4 MFMA's rate
 METRIC = "transform+MXFP4-quant GB/s (% HBM peak); MXFP4 GEMM TFLOPS (% MFMA peak)"
 METRIC_W4A8 = "transform+MXFP8-quant GB/s (% HBM peak); MXFP8 x MXFP4 GEMM TFLOP/s (% MFMA peak)"
+METRIC_KV = "KV-cache write (per-head transform + MX quant into cache slots) GB/s (% HBM peak)"
 METRIC_DECODE = "fused decode step (transform+MXFP4 quant in the GEMM prologue) GB/s (% HBM peak)"
 CACHE_BYTES = 256 * 2 ** 20
 
@@ -56,6 +57,8 @@ def parse():
                     help="fused decode step (w4a4_decode: activation path inside the GEMM), M <= 32 (config 4)")
     ap.add_argument("--graph", action="store_true",
                     help="with --decode: replay the steps from a captured HIP graph (no host launch overhead)")
+    ap.add_argument("--kv-cache", type=int, choices=[4, 8], default=None,
+                    help="KV-cache write of the config's tokens, 8 heads x 128 channels, MXFP4 (4) or MXFP8 (8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (HBM counter calibration)")
@@ -249,6 +252,81 @@ def run_decode(args, torch, w, wl, dev):
     print(json.dumps(out), flush=True)
 
 
+def run_kv(args, torch, w, wl, dev):
+    """KV-cache write: the config's tokens, 8 KV heads x 128 channels (the
+    key/value width of the pages' 8B model layers), through the per-head block
+    transform, clipping and MXFP4 / MXFP8 quantisation into permuted slots of a
+    cache four times as long.  Bound: HBM."""
+    from workloads import gen
+
+    T, HD = wl.M, 8 * 128
+    kv = gen.make_custom(T, HD, 8, seed=1000 * args.config + 77)
+    fmt = args.kv_cache
+    rows = 4 * T
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    X0 = torch.from_numpy(np.ascontiguousarray(kv.X_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    A, B = f32(kv.A), f32(kv.B)
+    rh = None if args.no_clip else f32(w.clip_ratios(kv.alpha))
+    rl = None if args.no_clip else f32(w.clip_ratios(kv.beta))
+    qcols = HD // 2 if fmt == 4 else HD
+    set_bytes = T * HD * 2 + rows * (qcols + HD // 32)
+    nsets = min(64, max(2, int(np.ceil(2.2 * CACHE_BYTES / set_bytes))))
+    rng = np.random.default_rng(5)
+    sets = [dict(X=X0.clone(), slots=torch.from_numpy(rng.permutation(rows)[:T].astype(np.int64)).to(dev),
+                 q=torch.zeros((rows, qcols), dtype=torch.uint8, device=dev),
+                 s=torch.zeros((rows, HD // 32), dtype=torch.uint8, device=dev)) for _ in range(nsets)]
+
+    def step(i):
+        st = sets[i % nsets]
+        w.kv_cache_quant(st["X"], A, B, rh, rl, st["slots"], st["q"], st["s"], fmt=fmt)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+    alg_bytes = T * HD * 2 + T * (qcols + HD // 32) + T * 8  # rows read, codes + scales written, slots read
+    gbs = alg_bytes / t_step / 1e9
+    out = {
+        "metric": METRIC_KV, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4" if fmt == 4 else "mxfp8", "data": "synthetic",
+        "config": {"workload": f"KV-cache write: {T} tokens x {HD} channels (8 heads x 128) bf16 (t3), GPK a=8 b=4, "
+                               f"{'MXFP4' if fmt == 4 else 'MXFP8 E4M3'} into permuted slots of a {rows}-row cache",
+                   "T": T, "HD": HD, "cache_rows": rows, "fmt": fmt, "buffer_sets": nsets, "clip": not args.no_clip},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": f"transform_quant_kernel<false,{'true' if fmt == 8 else 'false'}>"},
+        "kernels": {"kv_cache_quant": {"us": t_step * 1e6, "GB/s": gbs, "algorithmic_bytes": alg_bytes}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import batquant as ob
+
+        t_start, reps = time.perf_counter(), 0
+        while reps == 0 or (time.perf_counter() - t_start < args.cpu_min_seconds and reps < 8):
+            ob.kv_cache_quant(kv.X_bits, kv.A, kv.B, None if args.no_clip else kv.alpha,
+                              None if args.no_clip else kv.beta, fmt="e2m1" if fmt == 4 else "e4m3")
+            reps += 1
+        dt = (time.perf_counter() - t_start) / reps
+        import threadpoolctl
+
+        cores = max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": alg_bytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+                               "sample": f"the full write ({T} rows through the fp64 oracle path), {reps} repetition(s), "
+                                         f"{dt:.2f} s each"}
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(torch, dev, steps):
     """A plain elementwise copy of known size (fp32 negation: reads 1 GiB, writes
     1 GiB per launch), profiled with the same HBM counters as the kernels so
@@ -293,6 +371,9 @@ def main():
     M, K, N = wl.M, wl.K, wl.N
     if args.decode:
         run_decode(args, torch, w, wl, dev)
+        return
+    if args.kv_cache:
+        run_kv(args, torch, w, wl, dev)
         return
 
     def bf16(bits):

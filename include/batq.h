@@ -198,6 +198,31 @@ batq_status batq_act_transform_quant_mxfp8(const void* X_bf16, int64_t M, int64_
 batq_status batq_mxfp8_gemm_packed(const uint8_t* Xq8, const uint8_t* Xs, const uint8_t* Wp, int64_t M,
                                    int64_t N, int64_t K, void* Y, batq_out_dtype out, hipStream_t stream);
 
+/* ------------------------------------------------ KV-cache quantisation
+ * The pages place transforms on the key and value cache paths, per head, and
+ * report KV8 and KV4 settings (W4A8KV8, W4A8KV4) [en.papernotes.org, Overall
+ * Architecture; nubint.ai review, Table 2].  Here a token's K (or V) row,
+ * all heads side by side (HD = heads x head_dim channels, head_dim a multiple
+ * of 32 so that no block straddles two heads), goes through the same block
+ * transform, optional block-wise clipping and MX quantisation as activations,
+ * and is written to its cache slot.
+ */
+
+/* KV_bf16: [T][ld] bfloat16 new rows (ld >= HD, ld % 8 == 0, 16-byte aligned);
+ * A: [a][a], B: [HD/32][b][b] (one private factor per 32-channel block of each
+ * head); r_hi, r_lo: [HD/32] clip ratios or both NULL.  slots: [T] int64 device
+ * array (8-byte aligned), token t goes to cache row slots[t]; slots outside
+ * [0, cache_rows) are skipped, slots must be distinct.  fmt: 4 (MXFP4 E2M1
+ * codes, cache_q [cache_rows][HD/2]) or 8 (MXFP8 E4M3, cache_q
+ * [cache_rows][HD]); cache_s [cache_rows][HD/32] scales; cache_q 16-byte
+ * aligned.  Rows not named by a slot are left untouched.  T == 0 is a no-op.
+ * Errors: NULL, SHAPE (HD not a positive multiple of 32, negative sizes),
+ * ALIGN, UNSUPPORTED (factor size or fmt), HIP. */
+batq_status batq_kv_cache_quant(const void* KV_bf16, int64_t T, int64_t HD, int64_t ld, int32_t a, int32_t b,
+                                const float* A, const float* B, const float* r_hi, const float* r_lo,
+                                const int64_t* slots, int64_t cache_rows, int32_t fmt, uint8_t* cache_q,
+                                uint8_t* cache_s, hipStream_t stream);
+
 /* ------------------------------------------------ fused decode step
  * For decode-sized batches the online transform and quantisation run inside
  * the GEMM's prologue instead of as a separate launch [en.papernotes.org, Key

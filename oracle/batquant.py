@@ -407,6 +407,28 @@ def act_transform_quant(X_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
     return decisions(Y, S, rh, rl, exact=exact, fmt=fmt)
 
 
+def kv_cache_rows(slots: np.ndarray, cache_rows: int) -> np.ndarray:
+    """Placement of new K/V rows in a cache: input row t lands in cache row
+    slots[t]; a slot outside [0, cache_rows) places nothing.  Returns the input
+    row of every cache row (-1: not written)."""
+    src = np.full(cache_rows, -1, dtype=np.int64)
+    for t, r in enumerate(np.asarray(slots, dtype=np.int64)):
+        if 0 <= r < cache_rows:
+            src[r] = t
+    return src
+
+
+def kv_cache_quant(KV_bits: np.ndarray, A: np.ndarray, B: np.ndarray, alpha: Optional[np.ndarray],
+                   beta: Optional[np.ndarray], fmt: str = "e2m1", exact: bool = False) -> Decisions:
+    """K or V rows (all heads of a token side by side, head_dim a multiple of 32)
+    through the per-block transform, clipping and MX quantisation of the
+    activation path, MXFP4 (KV4) or MXFP8 E4M3 (KV8) [en.papernotes.org,
+    Overall Architecture: transforms on the key and value cache paths, per
+    head; nubint.ai review, Table 2: KV8, KV4].  The decisions are per input
+    row; kv_cache_rows gives their cache rows."""
+    return act_transform_quant(KV_bits, A, B, alpha, beta, exact=exact, fmt=fmt)
+
+
 def weight_prep(W_bits: np.ndarray, A: np.ndarray, B: np.ndarray,
                 walpha: Optional[np.ndarray], wbeta: Optional[np.ndarray],
                 exact: bool = False) -> Decisions:

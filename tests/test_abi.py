@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ("batq_act_transform_quant", "batq_weight_prep", "batq_mxfp4_gemm", "batq_gpk_invert",
               "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
               "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
-              "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode"):
+              "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode",
+              "batq_kv_cache_quant"):
         assert n in names
 
 
@@ -165,6 +166,27 @@ def test_decode_argument_checks(lib):
     # empty batch or no columns: no-ops that return before touching the GPU
     assert _dec(lib, M=0) == OK
     assert _dec(lib, N=0) == OK
+
+
+def _kv(lib, x=FAKE, T=4, HD=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0, slots=FAKE, rows=16, fmt=4,
+        q=FAKE, s=FAKE):
+    return lib.batq_kv_cache_quant(x, T, HD, ld, a, b, A, B, rh, rl, slots, rows, fmt, q, s, None)
+
+
+def test_kv_cache_argument_checks(lib):
+    assert _kv(lib, fmt=6) == UNSUP
+    assert _kv(lib, rows=-1) == SHAPE
+    assert _kv(lib, HD=48, ld=64) == SHAPE
+    assert _kv(lib, T=-1) == SHAPE
+    assert _kv(lib, a=8, b=8) == SHAPE
+    assert _kv(lib, slots=0) == NULL
+    assert _kv(lib, q=0) == NULL
+    assert _kv(lib, s=0) == NULL
+    assert _kv(lib, rh=FAKE) == NULL
+    assert _kv(lib, slots=FAKE + 4) == ALIGN
+    assert _kv(lib, q=FAKE + 8) == ALIGN
+    assert _kv(lib, x=FAKE + 2) == ALIGN
+    assert _kv(lib, T=0, slots=0) == OK
 
 
 def test_clip_ratios_match_oracle():

@@ -589,3 +589,11 @@ def test_mxfp8_quantisation_error_is_half_an_ulp():
     assert sat.any() and np.all(np.abs(d8)[sat] == 448.0 * scale[sat])
     c4, s4, _ = ob.clip_and_quantize(y, None, None, "e2m1")
     assert np.abs(ob.dequantize(c4, s4) - z).mean() > 3 * np.abs(d8 - z).mean()
+
+
+def test_kv_cache_rows_places_valid_slots_only():
+    """Cache placement: every in-range slot receives its token, out-of-range
+    slots place nothing, untouched rows stay unwritten (brute force by hand)."""
+    src = ob.kv_cache_rows(np.array([5, 0, -1, 9, 3, 10]), 10)
+    assert src.tolist() == [1, -1, -1, 4, -1, 0, -1, -1, -1, 3]
+    assert (ob.kv_cache_rows(np.array([], dtype=np.int64), 4) == -1).all()

@@ -25,4 +25,5 @@ from .binding import (  # noqa: F401
     decode_workspace,
     decode_workspace_bytes,
     w4a4_decode,
+    kv_cache_quant,
 )

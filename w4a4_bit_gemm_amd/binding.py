@@ -67,6 +67,8 @@ def _load():
                                                     P, P, P]
     lib.batq_mxfp8_gemm_packed.restype = ctypes.c_int
     lib.batq_mxfp8_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    lib.batq_kv_cache_quant.restype = ctypes.c_int
+    lib.batq_kv_cache_quant.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, I32, P, P, P]
     lib.batq_decode_workspace_bytes.restype = I64
     lib.batq_decode_workspace_bytes.argtypes = [I64, I64, I64]
     lib.batq_w4a4_decode.restype = ctypes.c_int
@@ -379,3 +381,28 @@ def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None
                                   _ptr(workspace), workspace.numel(), _stream_ptr(torch, X.device))
     _check(st)
     return out
+
+
+def kv_cache_quant(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s, fmt: int = 4):
+    """Quantise new K or V rows into a cache: KV [T, H*D] bf16 (head_dim a
+    multiple of 32), slots [T] int64 cache rows, cache_q [rows, H*D/2] (fmt 4,
+    MXFP4) or [rows, H*D] (fmt 8, MXFP8 E4M3) uint8, cache_s [rows, H*D/32]
+    uint8.  Rows of the cache not named by a slot are left untouched."""
+    torch = _torch()
+    _req(KV, torch.bfloat16, "KV")
+    _req(A, torch.float32, "A")
+    _req(B, torch.float32, "B")
+    _req(slots, torch.int64, "slots")
+    _req(cache_q, torch.uint8, "cache_q")
+    _req(cache_s, torch.uint8, "cache_s")
+    if (r_hi is None) != (r_lo is None):
+        raise ValueError("r_hi and r_lo must both be given or both be None")
+    T, HD = KV.shape
+    rows = cache_q.shape[0]
+    if fmt not in (4, 8) or tuple(cache_q.shape) != (rows, HD if fmt == 8 else HD // 2) \
+            or tuple(cache_s.shape) != (rows, HD // 32) or slots.numel() != T:
+        raise ValueError("cache / slot shapes do not match")
+    st = _load().batq_kv_cache_quant(_ptr(KV), T, HD, KV.stride(0), A.shape[0], B.shape[-1], _ptr(A), _ptr(B),
+                                     _ptr(r_hi), _ptr(r_lo), _ptr(slots), rows, fmt, _ptr(cache_q), _ptr(cache_s),
+                                     _stream_ptr(torch, KV.device))
+    _check(st)

@@ -80,7 +80,8 @@ batq_status check_transform_args(const void* x, int64_t rows, int64_t K, int64_t
 
 batq_status run_transform(const void* x, int64_t rows, int64_t K, int64_t ld, int32_t a, const float* A,
                           const float* B, const float* r_hi, const float* r_lo, int64_t r_ld, uint8_t* q,
-                          uint8_t* s, hipStream_t stream, int fp8 = 0) {
+                          uint8_t* s, hipStream_t stream, int fp8 = 0, const int64_t* slot = nullptr,
+                          int64_t out_rows = 0) {
   if (rows == 0) return BATQ_OK;
   batq::TransformQuantArgs args;
   args.x = static_cast<const uint16_t*>(x);
@@ -96,6 +97,8 @@ batq_status run_transform(const void* x, int64_t rows, int64_t K, int64_t ld, in
   args.q = q;
   args.s = s;
   args.fp8 = fp8;
+  args.slot = slot;
+  args.out_rows = out_rows;
   return batq::launch_transform_quant(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 
@@ -282,6 +285,20 @@ batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t l
   args.xs = Xs;
   args.part = static_cast<float*>(workspace);
   return batq::launch_decode_fused(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
+}
+
+batq_status batq_kv_cache_quant(const void* KV_bf16, int64_t T, int64_t HD, int64_t ld, int32_t a, int32_t b,
+                                const float* A, const float* B, const float* r_hi, const float* r_lo,
+                                const int64_t* slots, int64_t cache_rows, int32_t fmt, uint8_t* cache_q,
+                                uint8_t* cache_s, hipStream_t stream) {
+  if (cache_rows < 0) return BATQ_ERR_SHAPE;
+  if (fmt != 4 && fmt != 8) return BATQ_ERR_UNSUPPORTED;
+  const batq_status st = check_transform_args(KV_bf16, T, HD, ld, a, b, A, B, r_hi, r_lo, cache_q, cache_s);
+  if (st != BATQ_OK) return st;
+  if (T > 0 && slots == nullptr) return BATQ_ERR_NULL;
+  if (!aligned(slots, 8)) return BATQ_ERR_ALIGN;
+  return run_transform(KV_bf16, T, HD, ld, a, A, B, r_hi, r_lo, 0, cache_q, cache_s, stream, fmt == 8 ? 1 : 0, slots,
+                       cache_rows);
 }
 
 }  // extern "C"

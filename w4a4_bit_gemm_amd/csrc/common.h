@@ -39,6 +39,8 @@ struct TransformQuantArgs {
   uint8_t* q;           // [rows][K/2] (E2M1) or [rows][K] (E4M3)
   uint8_t* s;           // [rows][K/32]
   int fp8 = 0;          // 1: MXFP8 (E4M3) codes instead of MXFP4 (E2M1)
+  const int64_t* slot = nullptr;  // output row of each input row (KV cache), or nullptr: the row itself
+  int64_t out_rows = 0;           // rows of q / s when slot is set; other slots are skipped
 };
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream);
 

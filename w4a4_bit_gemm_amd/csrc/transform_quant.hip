@@ -225,6 +225,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
     block_barrier();                      // B_i
     if (wave == kStorerWave) {
+      // Output row of token tok: tok itself, or its cache slot (a slot outside
+      // [0, out_rows) is skipped).
+      auto out_row = [&](int64_t tok) -> int64_t {
+        if (p.slot == nullptr) return tok;
+        const int64_t r = p.slot[tok];
+        return r >= 0 && r < p.out_rows ? r : -1;
+      };
       // code bytes per row of the tile: 16 (E2M1) or 32 (E4M3) per block
       constexpr int kChunks = F8 ? 16 : 8;  // 16-byte chunks per staged row
 #pragma unroll
@@ -233,14 +240,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const int row = id / kChunks;
         const int c = id % kChunks;
         const int64_t tok = tok0 + row;
-        if (tok < p.rows && c / (kChunks / 8) < nblk)
-          *reinterpret_cast<uint4*>(p.q + tok * qld + blk0 * (2 * kChunks) + 16 * c) =
-              *reinterpret_cast<const uint4*>(qs + row * T::kQRow + 16 * c);
+        if (tok < p.rows && c / (kChunks / 8) < nblk) {
+          const int64_t orow = out_row(tok);
+          if (orow >= 0)
+            *reinterpret_cast<uint4*>(p.q + orow * qld + blk0 * (2 * kChunks) + 16 * c) =
+                *reinterpret_cast<const uint4*>(qs + row * T::kQRow + 16 * c);
+        }
       }
       if (lane < kTT) {
         const int64_t tok = tok0 + lane;
-        if (tok < p.rows) {
-          uint8_t* dst = p.s + tok * nb + blk0;
+        const int64_t orow = tok < p.rows ? out_row(tok) : -1;
+        if (orow >= 0) {
+          uint8_t* dst = p.s + orow * nb + blk0;
           const uint8_t* src = ss + lane * 8;
           if (nblk == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
             *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
