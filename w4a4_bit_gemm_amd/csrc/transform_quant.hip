@@ -133,17 +133,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int j = lane & 31;  // output channel (A-operand row) / token slot (B column)
   const int h = lane >> 5;  // which 8-channel half of each 16-channel k step
 
-  // P_i^T as MFMA A operand, exact three-way bf16 split.
-  const PSplit ps = build_p_split(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h);
-  // Ratios shared by every token (activations) are read once here.
-  const bool clip = p.r_hi != nullptr;
-  const bool per_row = PER_ROW && clip;
-  float rh_blk = 1.0f, rl_blk = 1.0f;
-  if (clip && !per_row && blk_ok) {
-    rh_blk = p.r_hi[blk];
-    rl_blk = p.r_lo[blk];
-  }
-
   const bool loader = wave == kLoaderWave;
   // Loader: tile i (< ntile) -> its slot, kTT / 2 load instructions per tile.
   // Addressing: a buffer descriptor based at the tile's first row whose
@@ -175,11 +164,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + q * 1024), 16, (int)voff[q & 7],
                                                (int)((q >> 3) * 16 * ld2), 0, 0);
   };
+  // The first tiles are requested before anything else, so that their latency
+  // overlaps the factor and ratio loads below (loads issued after them only
+  // make the loader's later waits stricter).
   if (loader) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the factor loads above are not counted below
     for (int i = 0; i < kRing - 1; ++i)
       if (i < ntile) load_tile(i, i);
   }
+
+  // P_i^T as MFMA A operand, exact three-way bf16 split.
+  const PSplit ps = build_p_split(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h);
+  // Ratios shared by every token (activations) are read once here.
+  const bool clip = p.r_hi != nullptr;
+  const bool per_row = PER_ROW && clip;
+  float rh_blk = 1.0f, rl_blk = 1.0f;
+  if (clip && !per_row && blk_ok) {
+    rh_blk = p.r_hi[blk];
+    rl_blk = p.r_lo[blk];
+  }
+
   static_assert(kRing == 4, "the loader's wait distinguishes 0, 1 or 2 younger tiles");
   const int64_t qld = F8 ? p.K : (p.K >> 1);
 
