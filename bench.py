@@ -475,12 +475,16 @@ def main():
                 "frac": act_gbs / HBM_PEAK_GBS}
     dominant_is_gemm = t_gemm.mean() >= t_act.mean()
     roof = dict(gemm_roof if dominant_is_gemm else act_roof)
-    gemm_src = "mxfp4_gemm_packed.hip" if packed else "mxfp4_gemm.hip"
     nst = K // 256
     gs = "true" if nst % 4 == 0 else "false"
     a8 = "true" if fp8 else "false"
-    gemm_kernel = (f"mxfp4_gemm_packed_kernel<{nst if nst in (1, 2, 4, 8, 16, 48) else 0},{gs},{a8}>" if packed
-                   else "mxfp4_gemm_dma_kernel")
+    if not packed:
+        gemm_src, gemm_kernel = "mxfp4_gemm.hip", "mxfp4_gemm_dma_kernel"
+    elif w.packed_gemm_kernel(M, N, K, fp8) == 1:  # the library's own choice for this shape
+        gemm_src, gemm_kernel = "mxfp4_gemm_packed_dma.hip", f"mxfp4_gemm_packed_dma_kernel<{nst}>"
+    else:
+        gemm_src = "mxfp4_gemm_packed.hip"
+        gemm_kernel = f"mxfp4_gemm_packed_kernel<{nst if nst in (1, 2, 4, 8, 16, 48) else 0},{gs},{a8}>"
     act_kernel = f"transform_quant_kernel<false,{a8}>"
     act_roof["traffic"] = load_traffic("transform_quant.hip", act_kernel, wl.name)
     gemm_roof["traffic"] = load_traffic(gemm_src, gemm_kernel, wl.name)

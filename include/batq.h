@@ -165,6 +165,14 @@ batq_status batq_weight_pack(const uint8_t* Wq, const uint8_t* Ws, int64_t N, in
 batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wp, int64_t M,
                                    int64_t N, int64_t K, void* Y, batq_out_dtype out, hipStream_t stream);
 
+/* Host-only query: which kernel batq_mxfp4_gemm_packed (act_fp8 == 0) or
+ * batq_mxfp8_gemm_packed (act_fp8 != 0) launches for this shape.  0: one
+ * 128 x 256 tile per workgroup, one workgroup per CU; 1: the same tiles and
+ * the same results bit for bit, two workgroups per CU with direct-to-LDS
+ * activation loads (more than 256 tiles, K / 256 in {4, 8, 16, 48}, E2M1
+ * activations under 2 GiB).  For profiling and reports; -1 on a bad shape. */
+int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8);
+
 /* ------------------------------------------------ W4A8: MXFP8 activations
  * The pages also report a W4A8 setting: MXFP8 activations against the same
  * MXFP4 weights [nubint.ai review, Table 2; en.papernotes.org, Experiments].

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
               "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
               "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode",
-              "batq_kv_cache_quant"):
+              "batq_kv_cache_quant", "batq_packed_gemm_kernel"):
         assert n in names
 
 
@@ -125,6 +125,21 @@ def test_packed_gemm_argument_checks(lib, name):
     assert f(FAKE, FAKE, FAKE, 4, 4, 256, FAKE + 2, 0, None) == ALIGN
     assert f(FAKE, FAKE, FAKE, 0, 4, 256, FAKE, 0, None) == OK
     assert f(FAKE, FAKE, FAKE, 4, 0, 256, FAKE, 1, None) == OK
+
+
+def test_packed_gemm_kernel_choice(lib):
+    """Two workgroups per CU only with more than 256 tiles of 128 x 256, a
+    compiled stage count (K / 256 in 4, 8, 16, 48) and E2M1 activations."""
+    f = lib.batq_packed_gemm_kernel
+    assert f(2048, 12288, 4096, 0) == 1                     # 16 x 48 tiles
+    assert f(16384, 4096, 4096, 0) == 1
+    assert f(2100, 4200, 12288, 0) == 1                     # 17 x 17 tiles
+    assert f(2048, 4096, 12288, 0) == 0                     # 16 x 16 = 256 tiles: one per CU
+    assert f(2048, 12288, 4096, 1) == 0                     # E4M3 activations
+    assert f(2048, 12288, 3072, 0) == 0 and f(2048, 12288, 512, 0) == 0  # runtime / small stage counts
+    assert f(1 << 20, 4096, 4096, 0) == 0                   # 2 GiB of activation codes
+    assert f(0, 12288, 4096, 0) == 0
+    assert f(4, 4, 100, 0) == -1 and f(-1, 4, 256, 0) == -1 and f(4, 4, 0, 0) == -1
 
 
 def test_decode_workspace_bytes(lib):

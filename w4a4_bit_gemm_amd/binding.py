@@ -62,6 +62,8 @@ def _load():
     lib.batq_weight_pack.argtypes = [P, P, I64, I64, P, P]
     lib.batq_mxfp4_gemm_packed.restype = ctypes.c_int
     lib.batq_mxfp4_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
+    lib.batq_packed_gemm_kernel.restype = I32
+    lib.batq_packed_gemm_kernel.argtypes = [I64, I64, I64, I32]
     lib.batq_act_transform_quant_mxfp8.restype = ctypes.c_int
     lib.batq_act_transform_quant_mxfp8.argtypes = [P, I64, I64, I64, ctypes.c_int32, ctypes.c_int32, P, P, P, P,
                                                     P, P, P]
@@ -324,6 +326,12 @@ def mxfp8_gemm_packed(Xq8, Xs, Wp: PackedWeight, out_dtype=None, out=None):
                                         _stream_ptr(torch, Xq8.device))
     _check(st)
     return out
+
+
+def packed_gemm_kernel(M: int, N: int, K: int, act_fp8: bool = False) -> int:
+    """Which kernel the packed GEMM launches for this shape (host-only query):
+    0 one workgroup per CU, 1 two per CU (same results); -1 bad shape."""
+    return int(_load().batq_packed_gemm_kernel(M, N, K, 1 if act_fp8 else 0))
 
 
 DECODE_MAX_M = 32

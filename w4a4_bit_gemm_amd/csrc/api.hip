@@ -244,6 +244,16 @@ batq_status batq_mxfp8_gemm_packed(const uint8_t* Xq8, const uint8_t* Xs, const 
 }
 
 
+int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8) {
+  if (M < 0 || N < 0 || K <= 0 || K % 256 != 0) return -1;
+  batq::GemmArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.a_fp8 = act_fp8 != 0;
+  return batq::packed_dma_applies(a) ? 1 : 0;
+}
+
 int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || K <= 0 || K % 256 != 0) return -1;
   return batq::decode_workspace_bytes(M, N, K);

@@ -66,6 +66,10 @@ hipError_t launch_weight_pack(const uint8_t* wq, const uint8_t* ws, int64_t N, i
                               hipStream_t stream);
 // Same GemmArgs; wq points at the packed buffer and ws is unused.
 hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream);
+// The two-workgroups-per-CU form of the same product (mxfp4_gemm_packed_dma.hip),
+// for the shapes where packed_dma_applies() holds.
+bool packed_dma_applies(const GemmArgs& args);
+hipError_t launch_mxfp4_gemm_packed_dma(const GemmArgs& args, hipStream_t stream);
 // Fused decode step (decode_fused.hip): transform + clip + MXFP4 quantisation
 // of M <= 32 tokens inside the GEMM on packed weights, split over
 // (256-column chunk, K split), then a split-order reduction launch.

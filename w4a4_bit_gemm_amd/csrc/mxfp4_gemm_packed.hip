@@ -550,6 +550,7 @@ hipError_t launch_weight_pack(const uint8_t* wq, const uint8_t* ws, int64_t N, i
 }
 
 hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream) {
+  if (packed_dma_applies(args)) return launch_mxfp4_gemm_packed_dma(args, stream);
   switch (args.K / 256) {
     case 1: return launch_packed<1, false>(args, stream);
     case 2: return launch_packed<2, false>(args, stream);

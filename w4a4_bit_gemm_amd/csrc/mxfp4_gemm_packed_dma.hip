@@ -1,0 +1,372 @@
+// W4A4 GEMM on packed weights, two workgroups per CU: Y = deq(Xq, Xs) deq(W)^T
+// with FP32 accumulation [BATQuant note (en.papernotes.org), Key Designs §1 and
+// §4: the product Q(XP) Q(P^-1 W^T) on block-scaled MXFP4 operands].
+//
+// Same tile (128 x 256), same operands and the same MFMA sequence per output
+// as the kernel in mxfp4_gemm_packed.hip, so the results are bit-identical;
+// what changes is how the data gets to the matrix cores.  With more than one
+// tile per CU, two resident workgroups cover each other's barrier waits and
+// LDS reads, which is worth 13-18 % on gfx950.  Two fit only if a workgroup
+// needs at most 256 registers per lane (128 accumulators + 128 others) and
+// 64 KB of LDS, so:
+//   activation codes  global -> LDS by 16-byte direct-to-LDS buffer loads (no
+//                     staging registers), two stages ahead, three-slot ring;
+//                     a row's 16-byte chunk c sits at position c ^ swz(row);
+//   activation scales the same way, four stages (32 bytes of a row) per load,
+//                     two-group ring;
+//   weights           packed, lane-ordered records straight into registers,
+//                     one stage ahead (two register sets);
+//   fragments         each sub-step's four activation fragments are read just
+//                     before its eight MFMAs (the other workgroup hides them).
+// Each wave waits only for its own loads (exact vmcnt), then one workgroup
+// barrier per stage publishes every wave's loads and frees the slot that the
+// next loads overwrite.  The output tile leaves through LDS (the ring).
+//
+// Needs a compile-time stage count K / 256 that is a multiple of 4, and
+// activations small enough for 32-bit buffer offsets (checked on the host).
+#include "common.h"
+
+namespace batq {
+
+namespace {
+
+constexpr int kMT = 4;                          // 32-row A tiles per wave
+constexpr int kNT = 2;                          // 32-column B tiles per wave
+constexpr int kBM = 32 * kMT;                   // 128 rows per tile
+constexpr int kBN = 4 * 32 * kNT;               // 256 columns, four waves along N
+constexpr int kRowBytes = 128;                  // activation code bytes per row and stage
+constexpr int kSlotBytes = kBM * kRowBytes;     // one stage of the tile's activations
+constexpr int kSGroupBytes = kBM * 32;          // scales of four stages
+constexpr int kEpiStride = 32 * kNT + 8;        // floats per staged output row
+constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes of one wave's staged 32-row band
+constexpr int kQPerWave = kSlotBytes / 1024 / 4;  // code DMA instructions per wave and stage (4)
+constexpr int kGroupM = 8;                      // row tiles per band of the tile order
+static_assert(2 * kEpiWave <= kSlotBytes + 4096, "two waves' epilogue bands fit one of the first two slots");
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ i32x8 op(uint4 v) {
+  i32x8 r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  return r;
+}
+template <int J>
+__device__ __forceinline__ f32x16 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb, f32x16 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(a), op(b), acc, 4, 4, J, (int)sa, J, (int)sb);
+}
+// A sub-step reads one 16-byte chunk of 32 consecutive rows per instruction;
+// this placement of chunk c of row r (c ^ swz(r)) measured fastest.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// Younger loads a step may leave in flight: a stage's code loads, plus the
+// scale-group load when one was issued after the weights.  n is a
+// compile-time constant once the stage loop is unrolled.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case kQPerWave: wait_vmcnt<kQPerWave>(); break;
+    case kQPerWave + 1: wait_vmcnt<kQPerWave + 1>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// Stage offsets pass through an empty asm so that the per-stage address
+// arithmetic stays in its pipeline step.
+__device__ __forceinline__ int64_t opaque_stage(int64_t s) {
+  asm volatile("" : "+s"(s));
+  return s;
+}
+
+#define DMA_DECL_B(n) \
+  uint4 n##_00, n##_01, n##_02, n##_03, n##_10, n##_11, n##_12, n##_13; \
+  uint32_t n##_s0, n##_s1;
+// Weight record of stage ST for both 32-column groups: four 1 KB code
+// sub-steps and the 256-byte scale block, 16 (4) bytes per lane.
+#define DMA_LOAD_B(n, ST)                                                                      \
+  {                                                                                            \
+    const int64_t off_ = opaque_stage(ST) * kPackGroupBytes;                                   \
+    const uint8_t* s0_ = b_base0 + off_;                                                       \
+    const uint8_t* s1_ = b_base1 + off_;                                                       \
+    n##_00 = ld16(s0_); n##_01 = ld16(s0_ + 1024); n##_02 = ld16(s0_ + 2048); n##_03 = ld16(s0_ + 3072); \
+    n##_s0 = ld4(s0_ + 4096 - 12 * lane);                                                      \
+    n##_10 = ld16(s1_); n##_11 = ld16(s1_ + 1024); n##_12 = ld16(s1_ + 2048); n##_13 = ld16(s1_ + 3072); \
+    n##_s1 = ld4(s1_ + 4096 - 12 * lane);                                                      \
+  }
+
+// Tile t of a tm x tn grid: consecutive workgroups go to the 8 XCDs in turn,
+// so XCD x receives a contiguous range of t, walked in bands of kGroupM row
+// tiles that share an activation panel in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int t, int tm, int tn, int& m, int& n) {
+  const int total = tm * tn;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int gsz = kGroupM * tn;
+  const int first = (t / gsz) * kGroupM;
+  const int gm = min(kGroupM, tm - first);
+  m = first + (t % gsz) % gm;
+  n = (t % gsz) / gm;
+}
+
+template <int NST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mxfp4_gemm_packed_dma_kernel(
+    GemmArgs p, int tiles_m, int tiles_n) {
+  static_assert(NST % 4 == 0, "scale groups span four stages");
+  // Separate arrays, so that the compiler sees which LDS reads each DMA can
+  // alias.  The first two slots also hold the epilogue's staged bands.
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes + 4096];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes + 4096];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sg0[kSGroupBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sg1[kSGroupBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kBM;
+  const int64_t c0 = (int64_t)tn * kBN;
+  const int64_t n0 = c0 + 64 * wave;  // this wave's first column
+  const int64_t n32_max = (p.N + 31) / 32;
+  // Each of the wave's two 32-column groups is clamped on its own: a clamped
+  // group is computed (so every wave reaches every barrier) but its columns
+  // lie past N and are never stored.
+  const int64_t n32_g0 = n0 / 32 < n32_max ? n0 / 32 : n32_max - 1;
+  const int64_t n32_g1 = n0 / 32 + 1 < n32_max ? n0 / 32 + 1 : n32_max - 1;
+  const uint8_t* const b_base0 = p.wq + (n32_g0 * NST) * kPackGroupBytes + 16 * lane;
+  const uint8_t* const b_base1 = p.wq + (n32_g1 * NST) * kPackGroupBytes + 16 * lane;
+
+  // Activation codes: instruction q of this wave fills LDS bytes
+  // [1024 (kQPerWave wave + q), +1024) = rows 8 (kQPerWave wave + q) + l / 8;
+  // lane l fetches the row's chunk (l % 8) ^ swz(row) for position l % 8.
+  // Rows past M read row M - 1 and are never stored.
+  const uint32_t krow = (uint32_t)(p.K >> 1);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, (short)0, (int)(p.M * (int64_t)krow), 0x00020000);
+  uint32_t qoff[kQPerWave];
+#pragma unroll
+  for (int q = 0; q < kQPerWave; ++q) {
+    const int row = 8 * (kQPerWave * wave + q) + (lane >> 3);
+    const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
+    qoff[q] = (uint32_t)gr * krow + 16u * (uint32_t)((lane & 7) ^ swz(row));
+  }
+  // Activation scales, four stages (32 bytes of a row) per group: wave w
+  // covers rows 32 w + l / 2, 16-byte half l % 2; LDS holds [row][32 bytes].
+  const uint32_t srow = (uint32_t)(p.K >> 5);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, (short)0, (int)(p.M * (int64_t)srow), 0x00020000);
+  uint32_t soff;
+  {
+    const int row = 32 * wave + (lane >> 1);
+    const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
+    soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane & 1);
+  }
+#define DMA_A(SLOT, ST)                                                                         \
+  _Pragma("unroll") for (int q = 0; q < kQPerWave; ++q)                                         \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)((SLOT) + 1024 * (kQPerWave * wave + q)), 16, \
+                                             (int)qoff[q], (int)((ST) * kRowBytes), 0, 0);
+#define DMA_S(SG, G) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)((SG) + 1024 * wave), 16, (int)soff, (int)((G) * 32), 0, 0);
+
+  f32x16 acc[kMT][kNT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) acc[i][k] = f32x16{};
+  DMA_DECL_B(b0)
+  DMA_DECL_B(b1)
+  // Issue order per wave: scale group 0, codes of stage 0, weights of stage
+  // 0, codes of stage 1; then each step S issues weights S + 1, the scale
+  // group that starts at S + 2 (if any) and codes S + 2.
+  DMA_S(sg0, 0)
+  DMA_A(slot0, 0)
+  DMA_LOAD_B(b0, 0)
+  DMA_A(slot1, 1)
+
+  // One sub-step j: the four activation fragments (rows 32 i + r32, chunk
+  // 4 g + j) from LDS, then 4 x 2 MFMAs.
+#define DMA_RD(SLOT, FO, I) *reinterpret_cast<const uint4*>((SLOT) + (FO) + 4096 * (I))
+#define DMA_SUB(SLOT, FO, J, n)                                                                \
+  {                                                                                            \
+    uint4 fa_[kMT];                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) fa_[i] = DMA_RD(SLOT, FO, i);              \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                          \
+      acc[i][0] = mfma_fp4<J>(fa_[i], n##_0##J, sa_[i], n##_s0, acc[i][0]);                   \
+      acc[i][1] = mfma_fp4<J>(fa_[i], n##_1##J, sa_[i], n##_s1, acc[i][1]);                   \
+    }                                                                                          \
+  }
+  // One stage; the lane parts of the LDS addresses are recomputed per stage
+  // (behind an empty asm) so that they are not held for every stage at once.
+#define DMA_MMA_STAGE(SLOT, SG, SQI, n)                                                         \
+  {                                                                                            \
+    uint32_t so_ = r32 * 32 + 4 * g;                                                           \
+    uint32_t fo0_ = r32 * kRowBytes + 16 * ((4 * g) ^ swz(r32));                                \
+    uint32_t fo1_ = r32 * kRowBytes + 16 * ((4 * g + 1) ^ swz(r32));                            \
+    uint32_t fo2_ = r32 * kRowBytes + 16 * ((4 * g + 2) ^ swz(r32));                            \
+    uint32_t fo3_ = r32 * kRowBytes + 16 * ((4 * g + 3) ^ swz(r32));                            \
+    asm volatile("" : "+v"(so_), "+v"(fo0_), "+v"(fo1_), "+v"(fo2_), "+v"(fo3_));              \
+    uint32_t sa_[kMT];                                                                         \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 8 * (SQI)); \
+    DMA_SUB(SLOT, fo0_, 0, n)                                                                  \
+    DMA_SUB(SLOT, fo1_, 1, n)                                                                  \
+    DMA_SUB(SLOT, fo2_, 2, n)                                                                  \
+    DMA_SUB(SLOT, fo3_, 3, n)                                                                  \
+  }
+  // Step S: wait for stage S (weights issued one step ago, codes two, scale
+  // group at least two), barrier, issue weights S + 1 then the loads of stage
+  // S + 2, compute stage S.
+#define DMA_STEP(S, CUR, NXT2, SG, SGN, BCUR, BNXT1)                                           \
+  {                                                                                            \
+    wait_vm(((S) + 1 < NST) ? (kQPerWave + (((S) + 1) % 4 == 0 ? 1 : 0)) : 0);                 \
+    block_barrier();                                                                           \
+    if ((S) + 1 < NST) { DMA_LOAD_B(BNXT1, (S) + 1) }                                          \
+    if ((S) + 2 < NST) {                                                                       \
+      if (((S) + 2) % 4 == 0) { DMA_S(SGN, ((S) + 2) / 4) }                                    \
+      DMA_A(NXT2, (S) + 2)                                                                     \
+    }                                                                                          \
+    sched_fence();                                                                             \
+    DMA_MMA_STAGE(CUR, SG, (S) % 4, BCUR)                                                      \
+  }
+  // Code slots cycle with period 3 (stage s in slot s % 3), weight sets with
+  // period 2, scale groups with period 8 (stage s reads group s / 4 from
+  // sg[(s / 4) % 2]; SGN is where the group starting at s + 2 goes): 24.
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    switch (s % 24) {
+      case 0: DMA_STEP(s, slot0, slot2, sg0, sg0, b0, b1) break;
+      case 1: DMA_STEP(s, slot1, slot0, sg0, sg0, b1, b0) break;
+      case 2: DMA_STEP(s, slot2, slot1, sg0, sg1, b0, b1) break;
+      case 3: DMA_STEP(s, slot0, slot2, sg0, sg1, b1, b0) break;
+      case 4: DMA_STEP(s, slot1, slot0, sg1, sg1, b0, b1) break;
+      case 5: DMA_STEP(s, slot2, slot1, sg1, sg1, b1, b0) break;
+      case 6: DMA_STEP(s, slot0, slot2, sg1, sg0, b0, b1) break;
+      case 7: DMA_STEP(s, slot1, slot0, sg1, sg0, b1, b0) break;
+      case 8: DMA_STEP(s, slot2, slot1, sg0, sg0, b0, b1) break;
+      case 9: DMA_STEP(s, slot0, slot2, sg0, sg0, b1, b0) break;
+      case 10: DMA_STEP(s, slot1, slot0, sg0, sg1, b0, b1) break;
+      case 11: DMA_STEP(s, slot2, slot1, sg0, sg1, b1, b0) break;
+      case 12: DMA_STEP(s, slot0, slot2, sg1, sg1, b0, b1) break;
+      case 13: DMA_STEP(s, slot1, slot0, sg1, sg1, b1, b0) break;
+      case 14: DMA_STEP(s, slot2, slot1, sg1, sg0, b0, b1) break;
+      case 15: DMA_STEP(s, slot0, slot2, sg1, sg0, b1, b0) break;
+      case 16: DMA_STEP(s, slot1, slot0, sg0, sg0, b0, b1) break;
+      case 17: DMA_STEP(s, slot2, slot1, sg0, sg0, b1, b0) break;
+      case 18: DMA_STEP(s, slot0, slot2, sg0, sg1, b0, b1) break;
+      case 19: DMA_STEP(s, slot1, slot0, sg0, sg1, b1, b0) break;
+      case 20: DMA_STEP(s, slot2, slot1, sg1, sg1, b0, b1) break;
+      case 21: DMA_STEP(s, slot0, slot2, sg1, sg1, b1, b0) break;
+      case 22: DMA_STEP(s, slot1, slot0, sg1, sg0, b0, b1) break;
+      default: DMA_STEP(s, slot2, slot1, sg1, sg0, b1, b0) break;
+    }
+  }
+#undef DMA_STEP
+#undef DMA_MMA_STAGE
+#undef DMA_SUB
+#undef DMA_RD
+#undef DMA_S
+#undef DMA_A
+
+  // The accumulators are final here: an empty asm that reads them keeps the
+  // last stages' MFMAs from sinking into the epilogue, which would keep their
+  // operands live across it.
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) asm volatile("" : "+a"(acc[i][k]));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  block_barrier();                     // every wave is done with the ring
+
+  // Epilogue through LDS: one 32-row band per pass, 16-byte row chunks out;
+  // waves 0, 1 stage in slot0 and waves 2, 3 in slot1.  Its inputs pass
+  // through an empty asm so that none of its address arithmetic is hoisted
+  // above the stage loop.
+  int lane_e = lane, wave_e = wave;
+  int64_t m0e = m0, c0e = c0;
+  asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
+  const int r32e = lane_e & 31, ge = lane_e >> 5;
+  float* epi = reinterpret_cast<float*>((wave_e < 2 ? slot0 : slot1) + (wave_e & 1) * kEpiWave);
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < kNT; ++k)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rs = 8 * (r >> 2) + 4 * ge + (r & 3);
+        epi[rs * kEpiStride + 32 * k + r32e] = acc[i][k][r];
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * 4 * kNT / 64; ++it) {
+      const int id = it * 64 + lane_e;
+      const int rs = id / (4 * kNT);
+      const int cc = id % (4 * kNT);
+      const float* src = epi + rs * kEpiStride + 8 * cc;
+      const float4 lo = reinterpret_cast<const float4*>(src)[0];
+      const float4 hi = reinterpret_cast<const float4*>(src)[1];
+      const int64_t row = m0e + 32 * i + rs;
+      const int64_t col = c0e + 64 * wave_e + 8 * cc;
+      if (row >= p.M || col >= p.N) continue;
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (p.out_f32) {
+        float* dst = reinterpret_cast<float*>(p.y) + row * p.N + col;
+        if (col + 8 <= p.N && p.vec_store) {
+          reinterpret_cast<float4*>(dst)[0] = lo;
+          reinterpret_cast<float4*>(dst)[1] = hi;
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = v[e];
+        }
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
+        uint32_t hb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hb[e] = f32_to_bf16_rne(v[e]);
+        if (col + 8 <= p.N && p.vec_store) {
+          *reinterpret_cast<uint4*>(dst) =
+              make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = (uint16_t)hb[e];
+        }
+      }
+    }
+  }
+}
+
+template <int NST>
+hipError_t launch_t(const GemmArgs& args, int tiles_m, int tiles_n, hipStream_t stream) {
+  hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Worth it once there is more than one tile per CU (256 CUs); needs a stage
+// count that is compiled here and byte offsets that fit the 32-bit buffer
+// descriptors.
+bool packed_dma_applies(const GemmArgs& a) {
+  if (a.a_fp8) return false;
+  const int64_t nst = a.K / 256;
+  if (nst != 4 && nst != 8 && nst != 16 && nst != 48) return false;
+  const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  return tiles > 256 && tiles < (int64_t)1 << 31 && a.M * (a.K >> 1) < (int64_t)1 << 31;
+}
+
+hipError_t launch_mxfp4_gemm_packed_dma(const GemmArgs& args, hipStream_t stream) {
+  const int tiles_m = (int)((args.M + kBM - 1) / kBM);
+  const int tiles_n = (int)((args.N + kBN - 1) / kBN);
+  switch (args.K / 256) {
+    case 4: return launch_t<4>(args, tiles_m, tiles_n, stream);
+    case 8: return launch_t<8>(args, tiles_m, tiles_n, stream);
+    case 16: return launch_t<16>(args, tiles_m, tiles_n, stream);
+    case 48: return launch_t<48>(args, tiles_m, tiles_n, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace batq
