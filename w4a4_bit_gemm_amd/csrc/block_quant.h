@@ -39,27 +39,45 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 struct PSplit {
   uint4 hi[2], mid[2], lo[2];
 };
-__device__ __forceinline__ PSplit build_p_split(const float* __restrict__ A, const float* __restrict__ Bi, int la,
-                                                int j, int h) {
+// The factor entries behind the lane's part of P_i^T:
+// P_i[k][j] = Bi[k / a][j / a] * A[k % a][j % a].  Loading is separate from
+// the split arithmetic so that a kernel can request these loads ahead of
+// bulk loads of its own (a wave's loads complete in issue order).
+struct PFactors {
+  float bv[2][8], av[2][8];
+};
+__device__ __forceinline__ PFactors load_p_factors(const float* __restrict__ A, const float* __restrict__ Bi, int la,
+                                                   int j, int h) {
   const int a = 1 << la;
   const int amask = a - 1;
   const int bdim = 32 >> la;
+  PFactors f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int k = 16 * ks + 8 * h + t;
+      f.bv[ks][t] = Bi[(k >> la) * bdim + (j >> la)];
+      f.av[ks][t] = A[(k & amask) * a + (j & amask)];
+    }
+  return f;
+}
+__device__ __forceinline__ PSplit split_p(const PFactors& f) {
   PSplit ps;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     uint32_t hw[8], mw[8], lw[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int k = 16 * ks + 8 * h + t;
-      const float bv = Bi[(k >> la) * bdim + (j >> la)];
-      const float av = A[(k & amask) * a + (j & amask)];
-      split3(bv, av, hw[t], mw[t], lw[t]);
-    }
+    for (int t = 0; t < 8; ++t) split3(f.bv[ks][t], f.av[ks][t], hw[t], mw[t], lw[t]);
     ps.hi[ks] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
     ps.mid[ks] = make_uint4(mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16);
     ps.lo[ks] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
   }
   return ps;
+}
+__device__ __forceinline__ PSplit build_p_split(const float* __restrict__ A, const float* __restrict__ Bi, int la,
+                                                int j, int h) {
+  return split_p(load_p_factors(A, Bi, la, j, h));
 }
 
 // y for one block and 32 tokens: x0 / x1 are the lane's 8 bf16 channels

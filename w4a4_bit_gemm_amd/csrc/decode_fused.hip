@@ -9,7 +9,11 @@
 //
 // decode_partial_kernel, one workgroup per (c, sp):
 //   1. every wave requests its weight records (its 64 columns, SPW stages)
-//      first, so that HBM latency overlaps everything below;
+//      before the transform, so that HBM latency overlaps it.  A wave's loads
+//      complete in issue order, so with one stage per workgroup the wave's
+//      activation-side loads (factor entries, token rows, ratios) go out just
+//      before the weights: the transform then waits only for them.  With
+//      more stages their registers would not fit, and they follow the weights;
 //   2. the workgroup transforms and quantises the split's activation blocks
 //      for all tokens with the same per-block arithmetic as the transform
 //      kernel (block_quant.h): the codes are identical bit for bit.  They are
@@ -36,6 +40,28 @@ __device__ __forceinline__ f32x16 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
+// Inputs of one activation block for the wave's 32 token slots: factor
+// entries, the lane's 16 channels of token j (zero for j >= M), the ratios.
+struct ActIn {
+  PFactors f;
+  uint4 x0, x1;
+  float rh, rl;
+};
+__device__ __forceinline__ ActIn load_act(const DecodeArgs& p, int64_t blk, int j, int h) {
+  const int bdim = 32 >> p.a_log2;
+  ActIn in;
+  in.f = load_p_factors(p.A, p.B + blk * bdim * bdim, p.a_log2, j, h);
+  in.x0 = in.x1 = make_uint4(0, 0, 0, 0);
+  if (j < p.M) {
+    const uint16_t* xr = p.x + (int64_t)j * p.ldx + blk * 32 + 8 * h;
+    in.x0 = *reinterpret_cast<const uint4*>(xr);
+    in.x1 = *reinterpret_cast<const uint4*>(xr + 16);
+  }
+  in.rh = p.r_hi ? p.r_hi[blk] : 1.0f;
+  in.rl = p.r_lo ? p.r_lo[blk] : 1.0f;
+  return in;
+}
+
 template <int SPW>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int nchunk, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[SPW][32 * kQRow];
@@ -48,6 +74,19 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int n
   const int sp = blockIdx.x / nchunk;
   const int64_t nst = p.K / 256;
   const int64_t s0 = (int64_t)sp * SPW;
+
+  // Wave w quantises blocks w and w + 4 of every stage of the split for
+  // tokens 0..31 (rows >= M are zero and never stored).
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  ActIn pre[2];
+  if constexpr (SPW == 1) {
+    if (s0 < nst) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) pre[bb] = load_act(p, s0 * 8 + wave + 4 * bb, j, h);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // 1. weight records of this wave's two 32-column groups for the split's
   // stages (stages past K are never requested).
@@ -72,11 +111,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int n
     }
   }
 
-  // 2. activation blocks: wave w quantises blocks w and w + 4 of every stage
-  // of the split for tokens 0..31 (rows >= M are zero and never stored).
-  const int j = lane & 31;
-  const int h = lane >> 5;
-  const int bdim = 32 >> p.a_log2;
+  if constexpr (SPW == 1) __builtin_amdgcn_sched_barrier(0);
+
+  // 2. activation blocks, staged in LDS in the MFMA operand order.
 #pragma unroll
   for (int t = 0; t < SPW; ++t) {
     if (s0 + t >= nst) break;
@@ -84,18 +121,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int n
     for (int bb = 0; bb < 2; ++bb) {
       const int lb = wave + 4 * bb;  // block within the stage
       const int64_t blk = (s0 + t) * 8 + lb;
-      const PSplit ps = build_p_split(p.A, p.B + blk * bdim * bdim, p.a_log2, j, h);
-      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
-      if (j < p.M) {
-        const uint16_t* xr = p.x + (int64_t)j * p.ldx + blk * 32 + 8 * h;
-        x0 = *reinterpret_cast<const uint4*>(xr);
-        x1 = *reinterpret_cast<const uint4*>(xr + 16);
-      }
-      const f32x16 acc = transform_block(ps, x0, x1);
-      const float rh = p.r_hi ? p.r_hi[blk] : 1.0f;
-      const float rl = p.r_lo ? p.r_lo[blk] : 1.0f;
+      const ActIn in = SPW == 1 ? pre[bb] : load_act(p, blk, j, h);
+      const f32x16 acc = transform_block(split_p(in.f), in.x0, in.x1);
       int sbyte;
-      const uint2 code = quant_block_e2m1(acc, rh, rl, h, sbyte);
+      const uint2 code = quant_block_e2m1(acc, in.rh, in.rl, h, sbyte);
       *reinterpret_cast<uint2*>(&qs[t][j * kQRow + 16 * lb + 8 * h]) = code;
       if (h == 0) ss[t][j * 8 + lb] = (uint8_t)sbyte;
       if (p.xq != nullptr && c == 0 && j < p.M) {  // optional copy of the quantised activations
