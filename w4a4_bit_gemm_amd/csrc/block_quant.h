@@ -19,16 +19,21 @@ namespace batq {
 
 typedef short v2i16 __attribute__((ext_vector_type(2)));
 
-// Exact product pa * pb split into three bf16 parts, hi + mid + lo, whose sum
-// differs from the product by at most ~2^-27 of it.
-__device__ __forceinline__ void split3(float pa, float pb, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  float r0 = pa * pb;
-  float e0 = __builtin_fmaf(pa, pb, -r0);  // exact rounding error of the product
-  hi = f32_to_bf16_rne(r0);
-  float rem = (r0 - bf16_to_f32(hi)) + e0;  // r0 - hi is exact
-  mid = f32_to_bf16_rne(rem);
-  float rem2 = rem - bf16_to_f32(mid);     // exact
-  lo = f32_to_bf16_rne(rem2);
+// Exact products pa0 * pb0 and pa1 * pb1, each split into three bf16 parts
+// hi + mid + lo whose sum differs from the product by at most ~2^-27 of it;
+// returned as packed pairs (product 0 in the low half).
+__device__ __forceinline__ void split3x2(float pa0, float pb0, float pa1, float pb1, uint32_t& hi, uint32_t& mid,
+                                         uint32_t& lo) {
+  const float r0 = pa0 * pb0, r1 = pa1 * pb1;
+  const float e0 = __builtin_fmaf(pa0, pb0, -r0);  // exact rounding errors of the products
+  const float e1 = __builtin_fmaf(pa1, pb1, -r1);
+  hi = f32x2_to_bf16x2_rne(r0, r1);
+  const float q0 = (r0 - __uint_as_float(hi << 16)) + e0;  // r - hi is exact
+  const float q1 = (r1 - __uint_as_float(hi & 0xFFFF0000u)) + e1;
+  mid = f32x2_to_bf16x2_rne(q0, q1);
+  const float s0 = q0 - __uint_as_float(mid << 16);  // exact
+  const float s1 = q1 - __uint_as_float(mid & 0xFFFF0000u);
+  lo = f32x2_to_bf16x2_rne(s0, s1);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -66,12 +71,13 @@ __device__ __forceinline__ PSplit split_p(const PFactors& f) {
   PSplit ps;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    uint32_t hw[8], mw[8], lw[8];
+    uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) split3(f.bv[ks][t], f.av[ks][t], hw[t], mw[t], lw[t]);
-    ps.hi[ks] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
-    ps.mid[ks] = make_uint4(mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16);
-    ps.lo[ks] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
+    for (int t = 0; t < 4; ++t)
+      split3x2(f.bv[ks][2 * t], f.av[ks][2 * t], f.bv[ks][2 * t + 1], f.av[ks][2 * t + 1], hw[t], mw[t], lw[t]);
+    ps.hi[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    ps.mid[ks] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    ps.lo[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   return ps;
 }

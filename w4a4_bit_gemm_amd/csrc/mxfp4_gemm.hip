@@ -55,15 +55,14 @@ __device__ __forceinline__ void store_out8(const GemmArgs& p, int64_t row, int64
     }
   } else {
     uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
-    uint32_t h[8];
+    uint32_t h[4];  // bf16 pairs
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(v[e]);
+    for (int e = 0; e < 4; ++e) h[e] = f32x2_to_bf16x2_rne(v[2 * e], v[2 * e + 1]);
     if (col + 8 <= p.N && p.vec_store) {
-      *reinterpret_cast<uint4*>(dst) =
-          make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
     } else {
       for (int e = 0; e < 8; ++e)
-        if (col + e < p.N) dst[e] = (uint16_t)h[e];
+        if (col + e < p.N) dst[e] = (uint16_t)(h[e >> 1] >> (16 * (e & 1)));
     }
   }
 }

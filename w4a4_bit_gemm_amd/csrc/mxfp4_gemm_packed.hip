@@ -511,15 +511,14 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
         }
       } else {
         uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
-        uint32_t hb[8];
+        uint32_t hb[4];  // bf16 pairs
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hb[e] = f32_to_bf16_rne(v[e]);
+        for (int e = 0; e < 4; ++e) hb[e] = f32x2_to_bf16x2_rne(v[2 * e], v[2 * e + 1]);
         if (col + 8 <= p.N && p.vec_store) {
-          *reinterpret_cast<uint4*>(dst) =
-              make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
+          *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
         } else {
           for (int e = 0; e < 8; ++e)
-            if (col + e < p.N) dst[e] = (uint16_t)hb[e];
+            if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
