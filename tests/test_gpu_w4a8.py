@@ -180,6 +180,35 @@ def test_w4a8_gemm_matches_oracle(w, M, N, K):
     assert np.array_equal(yb, parity.bf16_rne(y.astype(np.float32)).astype(np.float64))
 
 
+# More than 256 tiles of 128 x 256 with K / 256 in {4, 8, 16}: the two-
+# workgroups-per-CU kernel.  Rows are independent, so the output rows of a
+# slice of X (few tiles: the one-workgroup-per-CU kernel) must equal the same
+# rows of the full product bit for bit; sampled rows against the oracle.
+@pytest.mark.parametrize("M,N,K", [(2000, 12200, 1024), (2100, 8300, 2048), (2100, 4200, 4096)])
+def test_w4a8_gemm_two_workgroups_per_cu(w, M, N, K):
+    note(f"case: w4a8 gemm two workgroups per CU {M}x{N}x{K}")
+    assert w.packed_gemm_kernel(M, N, K, act_fp8=True) == 1
+    rng = np.random.default_rng(M + 3 * N + 5 * K)
+    xc, xs = _rand_e4m3(rng, M, K)
+    wc, ws = _rand_e2m1(rng, N, K)
+    wp = w.weight_pack(torch.from_numpy(ob.pack_codes(wc)).to(DEV), torch.from_numpy(ws).to(DEV))
+    X, XS = torch.from_numpy(xc).to(DEV), torch.from_numpy(xs).to(DEV)
+    Y = w.mxfp8_gemm_packed(X, XS, wp, out_dtype=torch.float32)
+    for r0, r1 in ((0, 256), (M - 200, M)):
+        assert w.packed_gemm_kernel(r1 - r0, N, K, act_fp8=True) == 0
+        Ys = w.mxfp8_gemm_packed(X[r0:r1].contiguous(), XS[r0:r1].contiguous(), wp, out_dtype=torch.float32)
+        assert torch.equal(Ys.view(torch.int32), Y[r0:r1].view(torch.int32)), (r0, r1)
+    rows = np.unique(np.concatenate([_sample_rows(M, 24, M + K), [M - 1]]))
+    ref = ob.gemm(xc[rows], xs[rows], wc, ws, x_fmt="e4m3")
+    bound = parity.w4a8_gemm_bound(xc[rows], xs[rows], wc, ws)
+    y = Y.cpu().numpy().astype(np.float64)[rows]
+    err = np.abs(y - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+    Yb = w.mxfp8_gemm_packed(X, XS, wp, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(Yb.float().cpu().numpy(), parity.bf16_rne(Y.cpu().numpy()))
+
+
 @pytest.mark.parametrize("M,N,K", [(5, 9, 256), (70, 61, 1024), (129, 257, 3072)])
 def test_w4a8_gemm_bit_exact_inside_the_window(w, M, N, K):
     """E4M3 exponent fields 6..9 (|x| in [0.5, 7.5]), unit scales: every product

@@ -110,6 +110,77 @@ __device__ __forceinline__ void tile_coords(int t, int tm, int tn, int& m, int& 
   n = (t % gsz) / gm;
 }
 
+// Output tile from the accumulators, through LDS (slot0 and slot1, both at
+// least 2 x kEpiWave bytes; the caller is done with them once every wave
+// reaches the barrier below).
+__device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT][kNT], int64_t m0, int64_t c0,
+                                           int wave, int lane, uint8_t* slot0, uint8_t* slot1) {
+  // The accumulators are final here: an empty asm that reads them keeps the
+  // last stages' MFMAs from sinking into the epilogue, which would keep their
+  // operands live across it.
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) asm volatile("" : "+a"(acc[i][k]));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  block_barrier();                     // every wave is done with the ring
+
+  // Epilogue through LDS: one 32-row band per pass, 16-byte row chunks out;
+  // waves 0, 1 stage in slot0 and waves 2, 3 in slot1.  Its inputs pass
+  // through an empty asm so that none of its address arithmetic is hoisted
+  // above the stage loop.
+  int lane_e = lane, wave_e = wave;
+  int64_t m0e = m0, c0e = c0;
+  asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
+  const int r32e = lane_e & 31, ge = lane_e >> 5;
+  float* epi = reinterpret_cast<float*>((wave_e < 2 ? slot0 : slot1) + (wave_e & 1) * kEpiWave);
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < kNT; ++k)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rs = 8 * (r >> 2) + 4 * ge + (r & 3);
+        epi[rs * kEpiStride + 32 * k + r32e] = acc[i][k][r];
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * 4 * kNT / 64; ++it) {
+      const int id = it * 64 + lane_e;
+      const int rs = id / (4 * kNT);
+      const int cc = id % (4 * kNT);
+      const float* src = epi + rs * kEpiStride + 8 * cc;
+      const float4 lo = reinterpret_cast<const float4*>(src)[0];
+      const float4 hi = reinterpret_cast<const float4*>(src)[1];
+      const int64_t row = m0e + 32 * i + rs;
+      const int64_t col = c0e + 64 * wave_e + 8 * cc;
+      if (row >= p.M || col >= p.N) continue;
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (p.out_f32) {
+        float* dst = reinterpret_cast<float*>(p.y) + row * p.N + col;
+        if (col + 8 <= p.N && p.vec_store) {
+          reinterpret_cast<float4*>(dst)[0] = lo;
+          reinterpret_cast<float4*>(dst)[1] = hi;
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = v[e];
+        }
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
+        uint32_t hb[4];  // bf16 pairs
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hb[e] = f32x2_to_bf16x2_rne(v[2 * e], v[2 * e + 1]);
+        if (col + 8 <= p.N && p.vec_store) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+}
+
 template <int NST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mxfp4_gemm_packed_dma_kernel(
     GemmArgs p, int tiles_m, int tiles_n) {
@@ -270,100 +341,209 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #undef DMA_S
 #undef DMA_A
 
-  // The accumulators are final here: an empty asm that reads them keeps the
-  // last stages' MFMAs from sinking into the epilogue, which would keep their
-  // operands live across it.
-#pragma unroll
-  for (int i = 0; i < kMT; ++i)
-#pragma unroll
-    for (int k = 0; k < kNT; ++k) asm volatile("" : "+a"(acc[i][k]));
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  block_barrier();                     // every wave is done with the ring
+  store_tile(p, acc, m0, c0, wave, lane, slot0, slot1);
+}
 
-  // Epilogue through LDS: one 32-row band per pass, 16-byte row chunks out;
-  // waves 0, 1 stage in slot0 and waves 2, 3 in slot1.  Its inputs pass
-  // through an empty asm so that none of its address arithmetic is hoisted
-  // above the stage loop.
-  int lane_e = lane, wave_e = wave;
-  int64_t m0e = m0, c0e = c0;
-  asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
-  const int r32e = lane_e & 31, ge = lane_e >> 5;
-  float* epi = reinterpret_cast<float*>((wave_e < 2 ? slot0 : slot1) + (wave_e & 1) * kEpiWave);
-#pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    sched_fence();
-#pragma unroll
-    for (int k = 0; k < kNT; ++k)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rs = 8 * (r >> 2) + 4 * ge + (r & 3);
-        epi[rs * kEpiStride + 32 * k + r32e] = acc[i][k][r];
-      }
-#pragma unroll
-    for (int it = 0; it < 32 * 4 * kNT / 64; ++it) {
-      const int id = it * 64 + lane_e;
-      const int rs = id / (4 * kNT);
-      const int cc = id % (4 * kNT);
-      const float* src = epi + rs * kEpiStride + 8 * cc;
-      const float4 lo = reinterpret_cast<const float4*>(src)[0];
-      const float4 hi = reinterpret_cast<const float4*>(src)[1];
-      const int64_t row = m0e + 32 * i + rs;
-      const int64_t col = c0e + 64 * wave_e + 8 * cc;
-      if (row >= p.M || col >= p.N) continue;
-      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (p.out_f32) {
-        float* dst = reinterpret_cast<float*>(p.y) + row * p.N + col;
-        if (col + 8 <= p.N && p.vec_store) {
-          reinterpret_cast<float4*>(dst)[0] = lo;
-          reinterpret_cast<float4*>(dst)[1] = hi;
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.N) dst[e] = v[e];
-        }
-      } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
-        uint32_t hb[4];  // bf16 pairs
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hb[e] = f32x2_to_bf16x2_rne(v[2 * e], v[2 * e + 1]);
-        if (col + 8 <= p.N && p.vec_store) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
-        }
-      }
-    }
-  }
+// E4M3 activations x packed E2M1 weights (the W4A8 setting): the same tile,
+// weights and scales, bit-identical to the E4M3 path of the packed kernel.
+// An activation row is 256 bytes per stage (32 KB per stage of the tile), so
+// the code ring has two slots (codes one stage ahead) to stay within 72 KB of
+// LDS per workgroup.  The row layout is that kernel's: 16-byte chunk c of row
+// r at position c ^ (r % 16).  The E4M3 operand of lane (r, g) in sub-step j
+// is chunks 2 j + g and 8 + 2 j + g of its row (see mfma_fp8_fp4).
+constexpr int kRowBytes8 = 256;
+constexpr int kSlotBytes8 = kBM * kRowBytes8;        // 32 KB
+constexpr int kQPerWave8 = kSlotBytes8 / 1024 / 4;   // 8 code DMA instructions per wave and stage
+static_assert(2 * kEpiWave <= kSlotBytes8, "two waves' epilogue bands fit one slot");
+
+template <int J>
+__device__ __forceinline__ f32x16 mfma_fp8_fp4(uint4 alo, uint4 ahi, uint4 b, uint32_t sa, uint32_t sb,
+                                               f32x16 acc) {
+  const i32x8 a = {(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op(b), acc, 0, 4, J, (int)sa, J, (int)sb);
 }
 
 template <int NST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w4a8_gemm_packed_dma_kernel(
+    GemmArgs p, int tiles_m, int tiles_n) {
+  static_assert(NST % 4 == 0, "scale groups span four stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes8];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes8];
+  __shared__ __attribute__((aligned(1024))) uint8_t sg0[kSGroupBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sg1[kSGroupBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kBM;
+  const int64_t c0 = (int64_t)tn * kBN;
+  const int64_t n0 = c0 + 64 * wave;
+  const int64_t n32_max = (p.N + 31) / 32;
+  const int64_t n32_g0 = n0 / 32 < n32_max ? n0 / 32 : n32_max - 1;
+  const int64_t n32_g1 = n0 / 32 + 1 < n32_max ? n0 / 32 + 1 : n32_max - 1;
+  const uint8_t* const b_base0 = p.wq + (n32_g0 * NST) * kPackGroupBytes + 16 * lane;
+  const uint8_t* const b_base1 = p.wq + (n32_g1 * NST) * kPackGroupBytes + 16 * lane;
+
+  // Codes: instruction q of this wave fills LDS bytes [1024 (8 wave + q),
+  // +1024) = rows 4 (8 wave + q) + l / 16; lane l fetches the row's chunk
+  // (l % 16) ^ (row % 16) for position l % 16.  The swizzle repeats every
+  // four instructions, so four lane offsets serve all eight, the rest of the
+  // row offset going into the scalar offset.  Rows past M lie past the end of
+  // the descriptor's range and read zeros; they are never stored.
+  const uint32_t krow = (uint32_t)p.K;
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, (short)0, (int)(p.M * (int64_t)krow), 0x00020000);
+  uint32_t qoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 4 * (kQPerWave8 * wave + q) + (lane >> 4);
+    qoff[q] = (uint32_t)(m0 + row) * krow + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+  }
+  const uint32_t srow = (uint32_t)(p.K >> 5);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, (short)0, (int)(p.M * (int64_t)srow), 0x00020000);
+  uint32_t soff;
+  {
+    const int row = 32 * wave + (lane >> 1);
+    const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
+    soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane & 1);
+  }
+  const uint32_t k16 = 16 * krow;  // 16 rows
+#define DMA_A8(SLOT, ST)                                                                        \
+  {                                                                                            \
+    const uint32_t st_ = (uint32_t)opaque_stage((ST) * kRowBytes8);                            \
+    _Pragma("unroll") for (int q = 0; q < kQPerWave8; ++q)                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)((SLOT) + 1024 * (kQPerWave8 * wave + q)), 16, \
+                                               (int)qoff[q & 3], (int)((q >> 2) * k16 + st_), 0, 0);        \
+  }
+#define DMA_S8(SG, G) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)((SG) + 1024 * wave), 16, (int)soff, (int)((G) * 32), 0, 0);
+
+  f32x16 acc[kMT][kNT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) acc[i][k] = f32x16{};
+  DMA_DECL_B(b0)
+  DMA_DECL_B(b1)
+  // Issue order per wave: scale group 0, codes and weights of stage 0; then
+  // step S issues the weights, the scale group starting at S + 1 (if any)
+  // and the codes of stage S + 1.  So each step waits for everything.
+  DMA_S8(sg0, 0)
+  DMA_A8(slot0, 0)
+  DMA_LOAD_B(b0, 0)
+
+  // Sub-step j: rows 32 i + r32, chunks 2 j + g and 8 + 2 j + g.  The lane
+  // offsets are recomputed per sub-step behind an empty asm, so that they are
+  // not all held across the stage loop.
+#define RD8(SLOT, I, FO) *reinterpret_cast<const uint4*>((SLOT) + 8192 * (I) + (FO))
+#define SUB8(SLOT, J, n)                                                                       \
+  {                                                                                            \
+    uint32_t flo_ = r32 * kRowBytes8 + 16 * ((2 * (J) + g) ^ (r32 & 15));                      \
+    uint32_t fhi_ = r32 * kRowBytes8 + 16 * ((8 + 2 * (J) + g) ^ (r32 & 15));                  \
+    asm volatile("" : "+v"(flo_), "+v"(fhi_));                                                 \
+    uint4 lo_[kMT], hi_[kMT];                                                                  \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                          \
+      lo_[i] = RD8(SLOT, i, flo_);                                                             \
+      hi_[i] = RD8(SLOT, i, fhi_);                                                             \
+    }                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                          \
+      acc[i][0] = mfma_fp8_fp4<J>(lo_[i], hi_[i], n##_0##J, sa_[i], n##_s0, acc[i][0]);       \
+      acc[i][1] = mfma_fp8_fp4<J>(lo_[i], hi_[i], n##_1##J, sa_[i], n##_s1, acc[i][1]);       \
+    }                                                                                          \
+  }
+#define MMA8_STAGE(SLOT, SG, SQI, n)                                                           \
+  {                                                                                            \
+    uint32_t so_ = r32 * 32 + 4 * g;                                                           \
+    asm volatile("" : "+v"(so_));                                                              \
+    uint32_t sa_[kMT];                                                                         \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 8 * (SQI)); \
+    SUB8(SLOT, 0, n)                                                                           \
+    SUB8(SLOT, 1, n)                                                                           \
+    SUB8(SLOT, 2, n)                                                                           \
+    SUB8(SLOT, 3, n)                                                                           \
+  }
+#define STEP8(S, CUR, NXT, SG, SGN, BCUR, BNXT)                                                \
+  {                                                                                            \
+    wait_vmcnt<0>();                                                                           \
+    block_barrier();                                                                           \
+    if ((S) + 1 < NST) {                                                                       \
+      DMA_LOAD_B(BNXT, (S) + 1)                                                                \
+      if (((S) + 1) % 4 == 0) { DMA_S8(SGN, ((S) + 1) / 4) }                                   \
+      DMA_A8(NXT, (S) + 1)                                                                     \
+    }                                                                                          \
+    sched_fence();                                                                             \
+    MMA8_STAGE(CUR, SG, (S) % 4, BCUR)                                                         \
+  }
+  // Stage s: codes in slot s % 2, weights in set s % 2, scales of group s / 4
+  // in sg[(s / 4) % 2]; SGN is where the group starting at s + 1 goes.
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    switch (s % 8) {
+      case 0: STEP8(s, slot0, slot1, sg0, sg0, b0, b1) break;
+      case 1: STEP8(s, slot1, slot0, sg0, sg0, b1, b0) break;
+      case 2: STEP8(s, slot0, slot1, sg0, sg0, b0, b1) break;
+      case 3: STEP8(s, slot1, slot0, sg0, sg1, b1, b0) break;
+      case 4: STEP8(s, slot0, slot1, sg1, sg1, b0, b1) break;
+      case 5: STEP8(s, slot1, slot0, sg1, sg1, b1, b0) break;
+      case 6: STEP8(s, slot0, slot1, sg1, sg1, b0, b1) break;
+      default: STEP8(s, slot1, slot0, sg1, sg0, b1, b0) break;
+    }
+  }
+#undef STEP8
+#undef MMA8_STAGE
+#undef SUB8
+#undef RD8
+#undef DMA_S8
+#undef DMA_A8
+
+  store_tile(p, acc, m0, c0, wave, lane, slot0, slot1);
+}
+
+template <int NST, bool A8>
 hipError_t launch_t(const GemmArgs& args, int tiles_m, int tiles_n, hipStream_t stream) {
-  hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
-                     tiles_m, tiles_n);
+  if constexpr (A8)
+    hipLaunchKernelGGL((w4a8_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+                       tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+                       tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Worth it once there is more than one tile per CU (256 CUs); needs a stage
-// count that is compiled here and byte offsets that fit the 32-bit buffer
+// count that is compiled here (E4M3 activations: 4, 8 or 16 stages, where the
+// kernel fits its registers) and byte offsets that fit the 32-bit buffer
 // descriptors.
 bool packed_dma_applies(const GemmArgs& a) {
-  if (a.a_fp8) return false;
   const int64_t nst = a.K / 256;
-  if (nst != 4 && nst != 8 && nst != 16 && nst != 48) return false;
+  if (nst != 4 && nst != 8 && nst != 16 && (a.a_fp8 || nst != 48)) return false;
   const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-  return tiles > 256 && tiles < (int64_t)1 << 31 && a.M * (a.K >> 1) < (int64_t)1 << 31;
+  const int64_t act_bytes = a.a_fp8 ? a.M * a.K : a.M * (a.K >> 1);
+  return tiles > 256 && tiles < (int64_t)1 << 31 && act_bytes < (int64_t)1 << 31;
 }
 
 hipError_t launch_mxfp4_gemm_packed_dma(const GemmArgs& args, hipStream_t stream) {
   const int tiles_m = (int)((args.M + kBM - 1) / kBM);
   const int tiles_n = (int)((args.N + kBN - 1) / kBN);
+  if (args.a_fp8) {
+    switch (args.K / 256) {
+      case 4: return launch_t<4, true>(args, tiles_m, tiles_n, stream);
+      case 8: return launch_t<8, true>(args, tiles_m, tiles_n, stream);
+      case 16: return launch_t<16, true>(args, tiles_m, tiles_n, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (args.K / 256) {
-    case 4: return launch_t<4>(args, tiles_m, tiles_n, stream);
-    case 8: return launch_t<8>(args, tiles_m, tiles_n, stream);
-    case 16: return launch_t<16>(args, tiles_m, tiles_n, stream);
-    case 48: return launch_t<48>(args, tiles_m, tiles_n, stream);
+    case 4: return launch_t<4, false>(args, tiles_m, tiles_n, stream);
+    case 8: return launch_t<8, false>(args, tiles_m, tiles_n, stream);
+    case 16: return launch_t<16, false>(args, tiles_m, tiles_n, stream);
+    case 48: return launch_t<48, false>(args, tiles_m, tiles_n, stream);
     default: return hipErrorInvalidValue;
   }
 }
