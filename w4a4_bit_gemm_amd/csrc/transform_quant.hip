@@ -279,6 +279,15 @@ hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t st
   int64_t gy = target / gx;
   if (gy >= 8) gy -= gy % 8;  // see the workgroup order in the kernel
   if (gy < 1) gy = 1;
+  // With fewer than 4 tiles each a workgroup's ring never fills (2048 x 4096:
+  // 10.1 us with 256 workgroups of 4 tiles, 11.1 us with 512 of 2), so fewer,
+  // longer workgroups are used as long as there remains one per CU (smaller
+  // grids measured slower).
+  int64_t cap = tiles / 4;
+  if (cap >= 8) cap -= cap % 8;
+  const int64_t one_per_cu = (256 + gx - 1) / gx;
+  if (cap < one_per_cu) cap = one_per_cu;
+  if (gy > cap) gy = cap;
   if (gy > tiles) gy = tiles;
   const dim3 grid((unsigned)(gx * gy));
   const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
