@@ -21,9 +21,12 @@
 // Each wave waits only for its own loads (exact vmcnt), then one workgroup
 // barrier per stage publishes every wave's loads and frees the slot that the
 // next loads overwrite.  The output tile leaves through LDS (the ring).
+// A second kernel does the same for E4M3 activations (the W4A8 setting), with
+// 256-byte rows and a two-slot ring (see w4a8_gemm_packed_dma_kernel).
 //
 // Needs a compile-time stage count K / 256 that is a multiple of 4, and
-// activations small enough for 32-bit buffer offsets (checked on the host).
+// activations small enough for 32-bit buffer offsets (packed_dma_applies
+// checks both on the host).
 #include "common.h"
 
 namespace batq {
