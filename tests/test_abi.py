@@ -149,8 +149,11 @@ def test_decode_workspace_bytes(lib):
     f = lib.batq_decode_workspace_bytes
     assert f(16, 4096, 4096) == 16 * 16 * 16 * 256 * 4      # one stage per K split
     assert f(1, 300, 512) == 2 * 2 * 1 * 256 * 4
-    assert f(4, 12288, 4096) == 48 * 8 * 4 * 256 * 4        # two stages per split
-    assert f(8, 12288, 12288) == 48 * 12 * 8 * 256 * 4      # four stages per split
+    assert f(4, 12288, 4096) == 48 * 16 * 4 * 256 * 4       # up to 16 tokens: one stage per split
+    assert f(8, 12288, 12288) == 48 * 48 * 8 * 256 * 4
+    assert f(32, 4096, 4096) == 16 * 16 * 32 * 256 * 4      # 256 workgroups: one stage
+    assert f(32, 12288, 4096) == 48 * 8 * 32 * 256 * 4      # more: two stages per split
+    assert f(17, 4096, 12288) == 16 * 24 * 17 * 256 * 4
     assert f(0, 256, 256) == 0
     assert f(33, 256, 256) == -1 and f(-1, 256, 256) == -1
     assert f(4, 256, 100) == -1 and f(4, 256, 0) == -1 and f(4, -1, 256) == -1

@@ -72,8 +72,10 @@ def test_decode_codes_match_oracle_and_transform_kernel(w, M, K, N, a, seed):
     parity.compare_quant(xq.cpu().numpy(), xs.cpu().numpy(), dec, label=f"decode {M}x{K}")
 
 
+# The last two shapes split K two stages per workgroup (more than 16 tokens
+# and more than 256 workgroups); the others one.
 @pytest.mark.parametrize("M,K,N,seed", [(1, 256, 256, 11), (7, 1024, 300, 12), (16, 4096, 4096, 13),
-                                        (32, 3072, 777, 14)])
+                                        (32, 3072, 777, 14), (32, 4096, 12288, 15), (17, 12288, 4096, 16)])
 def test_decode_gemm_exact_operands(w, M, K, N, seed):
     """Identity factors, no clipping and activations that are exact MXFP4 values
     (every block holds a +-6 code): the quantisation has no free decision, so

@@ -209,12 +209,14 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p, int nc
   }
 }
 
-// Stages per workgroup: enough workgroups to cover the machine (about 256),
-// as few partials as that allows.
-int stages_per_wg(int64_t nchunk, int64_t nst) {
-  if (nchunk * ((nst + 3) / 4) >= 256) return 4;
-  if (nchunk * ((nst + 1) / 2) >= 256) return 2;
-  return 1;
+// Stages per workgroup: one (the most workgroups, and each wave's activation
+// loads go out ahead of its weights) unless the fp32 partials would rival the
+// weights in bytes, i.e. above 16 tokens on grids of more than one workgroup
+// per CU: then two.  Measured on 1-32 tokens with K, N in {4096, 12288}: one
+// stage is 10-40 % faster up to 16 tokens; at 32 tokens two are 5-7 % faster
+// once there are more than 256 workgroups, and equal or slower below.
+int stages_per_wg(int64_t M, int64_t nchunk, int64_t nst) {
+  return (M <= 16 || nchunk * nst <= 256) ? 1 : 2;
 }
 
 template <int SPW>
@@ -230,19 +232,15 @@ hipError_t launch_t(const DecodeArgs& a, int nchunk, int nsplit, hipStream_t str
 
 int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t nchunk = (N + 255) / 256, nst = K / 256;
-  const int spw = stages_per_wg(nchunk, nst);
+  const int spw = stages_per_wg(M, nchunk, nst);
   return nchunk * ((nst + spw - 1) / spw) * M * 256 * 4;
 }
 
 hipError_t launch_decode_fused(const DecodeArgs& args, hipStream_t stream) {
   const int64_t nchunk = (args.N + 255) / 256, nst = args.K / 256;
-  const int spw = stages_per_wg(nchunk, nst);
+  const int spw = stages_per_wg(args.M, nchunk, nst);
   const int nsplit = (int)((nst + spw - 1) / spw);
-  switch (spw) {
-    case 4: return launch_t<4>(args, (int)nchunk, nsplit, stream);
-    case 2: return launch_t<2>(args, (int)nchunk, nsplit, stream);
-    default: return launch_t<1>(args, (int)nchunk, nsplit, stream);
-  }
+  return spw == 2 ? launch_t<2>(args, (int)nchunk, nsplit, stream) : launch_t<1>(args, (int)nchunk, nsplit, stream);
 }
 
 }  // namespace batq
