@@ -180,13 +180,13 @@ def test_w4a8_gemm_matches_oracle(w, M, N, K):
     assert np.array_equal(yb, parity.bf16_rne(y.astype(np.float32)).astype(np.float64))
 
 
-# More than 256 tiles of 128 x 256 with K / 256 in {4, 8, 16}: the two-
+# More than 256 tiles of 128 x 256 with K / 256 in {4, 8, 16, 48}: the two-
 # workgroups-per-CU kernel.  Rows are independent, so the output rows of a
 # slice of X (few tiles: the one-workgroup-per-CU kernel) must equal the same
 # rows of the full product bit for bit; sampled rows against the oracle.  N =
 # 33001: output rows that are not whole 16-byte chunks (scalar stores).
 @pytest.mark.parametrize("M,N,K", [(2000, 12200, 1024), (2100, 8300, 2048), (2100, 4200, 4096),
-                                   (1000, 33001, 1024)])
+                                   (2100, 4200, 12288), (1000, 33001, 1024)])
 def test_w4a8_gemm_two_workgroups_per_cu(w, M, N, K):
     note(f"case: w4a8 gemm two workgroups per CU {M}x{N}x{K}")
     assert w.packed_gemm_kernel(M, N, K, act_fp8=True) == 1
