@@ -170,8 +170,7 @@ batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const u
  * 128 x 256 tile per workgroup, one workgroup per CU; 1: the same tiles and
  * the same results bit for bit, two workgroups per CU with direct-to-LDS
  * activation loads (more than 256 tiles, K / 256 in {4, 8, 16, 48}, activation
- * codes and packed weights under 2 GiB each).  For profiling and reports; -1
- * on a bad shape. */
+ * codes under 2 GiB).  For profiling and reports; -1 on a bad shape. */
 int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8);
 
 /* ------------------------------------------------ W4A8: MXFP8 activations

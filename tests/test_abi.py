@@ -129,8 +129,8 @@ def test_packed_gemm_argument_checks(lib, name):
 
 def test_packed_gemm_kernel_choice(lib):
     """Two workgroups per CU only with more than 256 tiles of 128 x 256, a
-    compiled stage count (K / 256 in 4, 8, 16, 48), activation codes and packed
-    weights under 2 GiB each."""
+    compiled stage count (K / 256 in 4, 8, 16, 48) and activation codes under
+    2 GiB."""
     f = lib.batq_packed_gemm_kernel
     assert f(2048, 12288, 4096, 0) == 1                     # 16 x 48 tiles
     assert f(16384, 4096, 4096, 0) == 1
@@ -138,7 +138,7 @@ def test_packed_gemm_kernel_choice(lib):
     assert f(2048, 4096, 12288, 0) == 0                     # 16 x 16 = 256 tiles: one per CU
     assert f(2048, 12288, 4096, 1) == 1 and f(2100, 8300, 2048, 1) == 1  # E4M3 activations
     assert f(2100, 4200, 12288, 1) == 1                     # E4M3 with 48 stages
-    assert f(2048, 1 << 20, 4096, 0) == 0                   # 2.2 GB of packed weights
+    assert f(2048, 1 << 20, 4096, 0) == 1                   # 2.2 GB of packed weights: per-group descriptors
     assert f(2048, 12288, 3072, 0) == 0 and f(2048, 12288, 512, 0) == 0  # runtime / small stage counts
     assert f(1 << 20, 4096, 4096, 0) == 0                   # 2 GiB of activation codes
     assert f(1 << 19, 4096, 4096, 1) == 0 and f((1 << 19) - 128, 4096, 4096, 1) == 1

@@ -101,20 +101,22 @@ __device__ __forceinline__ int64_t opaque_stage(int64_t s) {
 // sub-steps and the 256-byte scale block, 16 (4) bytes per lane.
 #define DMA_LOAD_B(n, ST)                                                                      \
   {                                                                                            \
-    const int o0_ = (int)((n32_g0 * NST + opaque_stage(ST)) * kPackGroupBytes);                \
-    const int o1_ = (int)((n32_g1 * NST + opaque_stage(ST)) * kPackGroupBytes);                \
-    n##_00 = bl16(wrs, lane16, o0_); n##_01 = bl16(wrs, lane16, o0_ + 1024);                   \
-    n##_02 = bl16(wrs, lane16, o0_ + 2048); n##_03 = bl16(wrs, lane16, o0_ + 3072);            \
-    n##_s0 = bl4(wrs, lane4, o0_ + 4096);                                                      \
-    n##_10 = bl16(wrs, lane16, o1_); n##_11 = bl16(wrs, lane16, o1_ + 1024);                   \
-    n##_12 = bl16(wrs, lane16, o1_ + 2048); n##_13 = bl16(wrs, lane16, o1_ + 3072);            \
-    n##_s1 = bl4(wrs, lane4, o1_ + 4096);                                                      \
+    const int o_ = (int)(opaque_stage(ST) * kPackGroupBytes);                                  \
+    n##_00 = bl16(wrs0, lane16, o_); n##_01 = bl16(wrs0, lane16, o_ + 1024);                   \
+    n##_02 = bl16(wrs0, lane16, o_ + 2048); n##_03 = bl16(wrs0, lane16, o_ + 3072);            \
+    n##_s0 = bl4(wrs0, lane4, o_ + 4096);                                                      \
+    n##_10 = bl16(wrs1, lane16, o_); n##_11 = bl16(wrs1, lane16, o_ + 1024);                   \
+    n##_12 = bl16(wrs1, lane16, o_ + 2048); n##_13 = bl16(wrs1, lane16, o_ + 3072);            \
+    n##_s1 = bl4(wrs1, lane4, o_ + 4096);                                                      \
   }
-// Descriptor over the packed weights (under 2 GiB: checked on the host) and
-// the lane offsets of a record's code (16 l) and scale (4 l) bytes.
+// One descriptor per 32-column group, based at its first record (a group's
+// NST records stay under 2 GiB: checked on the host), and the lane offsets of
+// a record's code (16 l) and scale (4 l) bytes.
 #define DECL_WEIGHTS                                                                           \
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(                        \
-      (void*)p.wq, (short)0, (int)(n32_max * NST * kPackGroupBytes), 0x00020000);               \
+  const __amdgpu_buffer_rsrc_t wrs0 = __builtin_amdgcn_make_buffer_rsrc(                       \
+      (void*)(p.wq + n32_g0 * NST * kPackGroupBytes), (short)0, NST * (int)kPackGroupBytes, 0x00020000); \
+  const __amdgpu_buffer_rsrc_t wrs1 = __builtin_amdgcn_make_buffer_rsrc(                       \
+      (void*)(p.wq + n32_g1 * NST * kPackGroupBytes), (short)0, NST * (int)kPackGroupBytes, 0x00020000); \
   const uint32_t lane16 = 16u * (uint32_t)lane, lane4 = 4u * (uint32_t)lane;
 
 // Tile t of a tm x tn grid: consecutive workgroups go to the 8 XCDs in turn,
@@ -535,15 +537,14 @@ hipError_t launch_t(const GemmArgs& args, int tiles_m, int tiles_n, hipStream_t 
 }  // namespace
 
 // Worth it once there is more than one tile per CU (256 CUs); needs a stage
-// count that is compiled here and activations and packed weights small enough
-// for the 32-bit offsets of buffer descriptors.
+// count that is compiled here and activations small enough for the 32-bit
+// offsets of a buffer descriptor.
 bool packed_dma_applies(const GemmArgs& a) {
   const int64_t nst = a.K / 256;
   if (nst != 4 && nst != 8 && nst != 16 && nst != 48) return false;
   const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
   const int64_t act_bytes = a.a_fp8 ? a.M * a.K : a.M * (a.K >> 1);
-  const int64_t w_bytes = ((a.N + 31) / 32) * nst * kPackGroupBytes;
-  return tiles > 256 && tiles < (int64_t)1 << 31 && act_bytes < (int64_t)1 << 31 && w_bytes < (int64_t)1 << 31;
+  return tiles > 256 && tiles < (int64_t)1 << 31 && act_bytes < (int64_t)1 << 31;
 }
 
 hipError_t launch_mxfp4_gemm_packed_dma(const GemmArgs& args, hipStream_t stream) {
