@@ -454,6 +454,53 @@ def test_packed_end_to_end_full_config(w, cfg):
 
 
 
+
+@pytest.mark.parametrize("M,N,K", [(2048, 4200, 1024), (100, 300, 512)])
+def test_step_graph_replays_match_eager(w, M, N, K):
+    """The online step (transform + clip + MXFP4 quantisation, then the packed
+    GEMM) captured in a HIP graph: every one of several replays, with eager
+    work and synchronisations between them, equals the eager result bit for
+    bit (no library call records a memset).  The first shape runs the
+    two-workgroups-per-CU GEMM, the second the one-per-CU kernel."""
+    note(f"case: step graph replay {M}x{N}x{K}")
+    assert w.packed_gemm_kernel(M, N, K) == (1 if M == 2048 else 0)
+    wl = gen.make_custom(M, K, N, seed=M + N)
+    X = dev_bf16(wl.X_bits)
+    A, B = dev_f32(wl.A), dev_f32(wl.B)
+    rh, rl = dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta))
+    wq, wsc = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    Wp = w.weight_pack(wq, wsc)
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    Xs = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        w.act_transform_quant(X, A, B, rh, rl, out=(Xq, Xs))
+        w.mxfp4_gemm_packed(Xq, Xs, Wp, out=Y)
+
+    step()
+    torch.cuda.synchronize()
+    eager = Y.clone()
+    other = dev_bf16(np.ascontiguousarray(wl.X_bits[::-1]))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        Y.fill_(float("nan"))
+        Xq.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), eager.view(torch.int16)), rep
+        oq, os_ = w.act_transform_quant(other, A, B, rh, rl)  # eager work between replays
+        w.mxfp4_gemm_packed(oq, os_, Wp, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+
 # ------------------------------------------- block-Hadamard (BRQ) special case
 
 
