@@ -39,10 +39,10 @@ namespace {
 
 constexpr int kBlocksPerWG = 8;  // one 32-channel block per compute wave; 8 blocks = 128 code bytes per row
 constexpr int kLoaderWave = kBlocksPerWG - 1;  // also issues the global -> LDS tile loads
-constexpr int kStorerWave = kBlocksPerWG - 2;  // also writes the staged codes and scales
+constexpr int kStorerWaves = 4;                // waves 0-3 also write the staged codes and scales
 constexpr int kThreads = 64 * kBlocksPerWG;
 constexpr int kTT = 32;                        // tokens per tile (one MFMA group)
-constexpr int kRing = 4;                       // LDS tile slots; kRing - 1 tiles in flight
+static_assert(kLoaderWave >= kStorerWaves, "the loader issues no stores");
 
 __device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -79,24 +79,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 // tiles ty = y, y + gy, ... (32 tokens each), with
 // two workgroups resident per CU.  Every wave w computes block blk0 + w: it
 // builds its P_i split once, then per tile runs the MFMA transform, clip,
-// scale and E2M1 codes into LDS staging buffers.  Two waves have a second
-// role, chosen so that no wave's memory-counter waits ever cover another
-// kind of traffic:
+// scale and codes into one of two LDS staging buffers.  Waves also have a
+// second role, chosen so that no wave's memory-counter waits ever cover
+// another kind of traffic:
 //   loader (wave 7)   keeps kRing - 1 tiles in flight: 16-byte direct-to-LDS
 //                     loads, one instruction = two whole 512-byte row segments;
 //                     row r keeps its 16-byte chunk c at position c ^ (r & 15),
 //                     so the MFMA operand reads (16 consecutive rows, same
 //                     chunk) hit 16 different bank groups.  It issues no
 //                     stores, so its wait for a tile is an exact count;
-//   storer (wave 6)   writes the staged codes as 16-byte row-contiguous chunks
-//                     (whole 128-byte lines per row) and the scales as 8-byte
-//                     row pieces.  It never waits for its stores.
-// Per tile i, two workgroup barriers: A_i (tile i is in LDS; staging is free)
-// and B_i (tile i's codes and scales are staged).
+//   storers (0-3)     after computing tile i, wave w writes rows 8 w .. 8 w + 7
+//                     of tile i - 1's staged codes as 16-byte row-contiguous
+//                     chunks (whole 128-byte lines per row) and its scales as
+//                     8-byte row pieces.  They never wait for their stores.
+// One workgroup barrier per tile, X_i: tile i is in its slot, tile i - 1 is
+// staged (and may be stored), tile i - 2's staging has been stored (its
+// buffer takes tile i).  With a single staging buffer it took two (measured
+// 4-6 % slower).
 template <bool F8>
 struct TQSmem {
   static constexpr int kXRow = 512;        // bytes per staged bf16 row (256 channels)
   static constexpr int kX = kTT * kXRow;   // one tile slot
+  // LDS tile slots (kRing - 1 tiles in flight): E4M3 staging is twice as
+  // large, and two workgroups per CU must still fit (4 x 16 + 2 x 8.5 KB would not).
+  static constexpr int kRing = F8 ? 3 : 4;
   // staged code row: 128 (E2M1) or 256 (E4M3) bytes + 16 pad, conflict-free writes
   static constexpr int kQRow = F8 ? 272 : 144;
 };
@@ -109,9 +115,10 @@ template <bool PER_ROW, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
     TransformQuantArgs p, int64_t gy) {
   using T = TQSmem<F8>;
+  constexpr int kRing = T::kRing;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kRing * T::kX];
-  __shared__ __attribute__((aligned(16))) uint8_t qs[kTT * T::kQRow];
-  __shared__ __attribute__((aligned(16))) uint8_t ss[kTT * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[2 * kTT * T::kQRow];  // two staging buffers
+  __shared__ __attribute__((aligned(16))) uint8_t ss[2 * kTT * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,25 +190,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     rl_blk = p.r_lo[blk];
   }
 
-  static_assert(kRing == 4, "the loader's wait distinguishes 0, 1 or 2 younger tiles");
+  static_assert(kRing == 3 || kRing == 4, "the loader's wait distinguishes up to 2 younger tiles");
   const int64_t qld = F8 ? p.K : (p.K >> 1);
+
+  // Output row of token tok: tok itself, or its cache slot (a slot outside
+  // [0, out_rows) is skipped).
+  auto out_row = [&](int64_t tok) -> int64_t {
+    if (p.slot == nullptr) return tok;
+    const int64_t r = p.slot[tok];
+    return r >= 0 && r < p.out_rows ? r : -1;
+  };
+  // Storer wave w: rows 8 w .. 8 w + 7 of tile ti's codes and scales from
+  // staging buffer sb; 16 (E2M1) or 32 (E4M3) code bytes per block and row.
+  auto store_rows = [&](int64_t ti, int sb) {
+    constexpr int kChunks = F8 ? 16 : 8;  // 16-byte chunks per staged row
+    const int64_t tok0 = (ty0 + ti * tstep) * kTT;
+    const uint8_t* qsb = qs + sb * kTT * T::kQRow;
+#pragma unroll
+    for (int k = 0; k < kChunks / 8; ++k) {
+      const int id = lane + 64 * k;
+      const int row = 8 * wave + id / kChunks;
+      const int c = id % kChunks;
+      const int64_t tok = tok0 + row;
+      if (tok < p.rows && c / (kChunks / 8) < nblk) {
+        const int64_t orow = out_row(tok);
+        if (orow >= 0)
+          *reinterpret_cast<uint4*>(p.q + orow * qld + blk0 * (2 * kChunks) + 16 * c) =
+              *reinterpret_cast<const uint4*>(qsb + row * T::kQRow + 16 * c);
+      }
+    }
+    if (lane < 8) {
+      const int row = 8 * wave + lane;
+      const int64_t tok = tok0 + row;
+      const int64_t orow = tok < p.rows ? out_row(tok) : -1;
+      if (orow >= 0) {
+        uint8_t* dst = p.s + orow * nb + blk0;
+        const uint8_t* src = ss + sb * kTT * 8 + row * 8;
+        if (nblk == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+        } else {
+          for (int c = 0; c < nblk; ++c) dst[c] = src[c];
+        }
+      }
+    }
+  };
 
   for (int64_t i = 0; i < ntile; ++i) {
     if (loader) {
       // tile i has landed once at most the younger tiles' loads are pending
       const int64_t younger = ntile - 1 - i;
-      if (younger >= 2) {
+      if (younger >= 2 && kRing == 4) {
         wait_vmcnt<2 * (kTT / 2)>();
-      } else if (younger == 1) {
+      } else if (younger >= 1) {
         wait_vmcnt<kTT / 2>();
       } else {
         wait_vmcnt<0>();
       }
     }
-    block_barrier();  // A_i: tile i is in its slot; the previous staging has been read
+    block_barrier();  // X_i
     if (loader && i + kRing - 1 < ntile) load_tile(i + kRing - 1, (int)((i + kRing - 1) % kRing));
-    const int64_t tok0 = (ty0 + i * tstep) * kTT;
+    const int sb = (int)(i & 1);
     if (blk_ok) {
+      const int64_t tok0 = (ty0 + i * tstep) * kTT;
       const uint8_t* xt = xs + (int)(i % kRing) * T::kX;
       const int row = j;
       const uint8_t* xr = xt + row * T::kXRow;
@@ -217,53 +267,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         rh = p.r_hi[ri];
         rl = p.r_lo[ri];
       }
+      uint8_t* qsb = qs + sb * kTT * T::kQRow;
       int sbyte;
       if constexpr (F8) {
-        *reinterpret_cast<uint4*>(qs + row * T::kQRow + 32 * wave + 16 * h) = quant_block_e4m3(acc, rh, rl, h, sbyte);
+        *reinterpret_cast<uint4*>(qsb + row * T::kQRow + 32 * wave + 16 * h) = quant_block_e4m3(acc, rh, rl, h, sbyte);
       } else {
-        *reinterpret_cast<uint2*>(qs + row * T::kQRow + 16 * wave + 8 * h) = quant_block_e2m1(acc, rh, rl, h, sbyte);
+        *reinterpret_cast<uint2*>(qsb + row * T::kQRow + 16 * wave + 8 * h) = quant_block_e2m1(acc, rh, rl, h, sbyte);
       }
-      if (h == 0) ss[row * 8 + wave] = (uint8_t)sbyte;
+      if (h == 0) ss[sb * kTT * 8 + row * 8 + wave] = (uint8_t)sbyte;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-    block_barrier();                      // B_i
-    if (wave == kStorerWave) {
-      // Output row of token tok: tok itself, or its cache slot (a slot outside
-      // [0, out_rows) is skipped).
-      auto out_row = [&](int64_t tok) -> int64_t {
-        if (p.slot == nullptr) return tok;
-        const int64_t r = p.slot[tok];
-        return r >= 0 && r < p.out_rows ? r : -1;
-      };
-      // code bytes per row of the tile: 16 (E2M1) or 32 (E4M3) per block
-      constexpr int kChunks = F8 ? 16 : 8;  // 16-byte chunks per staged row
-#pragma unroll
-      for (int k = 0; k < kTT * kChunks / 64; ++k) {
-        const int id = lane + 64 * k;
-        const int row = id / kChunks;
-        const int c = id % kChunks;
-        const int64_t tok = tok0 + row;
-        if (tok < p.rows && c / (kChunks / 8) < nblk) {
-          const int64_t orow = out_row(tok);
-          if (orow >= 0)
-            *reinterpret_cast<uint4*>(p.q + orow * qld + blk0 * (2 * kChunks) + 16 * c) =
-                *reinterpret_cast<const uint4*>(qs + row * T::kQRow + 16 * c);
-        }
-      }
-      if (lane < kTT) {
-        const int64_t tok = tok0 + lane;
-        const int64_t orow = tok < p.rows ? out_row(tok) : -1;
-        if (orow >= 0) {
-          uint8_t* dst = p.s + orow * nb + blk0;
-          const uint8_t* src = ss + lane * 8;
-          if (nblk == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
-          } else {
-            for (int c = 0; c < nblk; ++c) dst[c] = src[c];
-          }
-        }
-      }
-    }
+    if (wave < kStorerWaves && i > 0) store_rows(i - 1, sb ^ 1);
+  }
+  if (ntile > 0) {
+    block_barrier();  // the last tile is staged
+    if (wave < kStorerWaves) store_rows(ntile - 1, (int)((ntile - 1) & 1));
   }
 }
 
