@@ -38,7 +38,6 @@ constexpr int kBN = 4 * 32 * kNT;  // 256, four waves along N
 constexpr int kRowBytes = 128;
 constexpr int kAStage = kBM * kRowBytes;        // 16 KB
 constexpr int kAScale = kBM * 8;                // 1 KB
-constexpr int kSlot = kAStage + kAScale;
 constexpr int kEpiStride = 32 * kNT + 8;        // floats
 constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes
 constexpr int kGroupM = 8;                      // row tiles per band of the tile order

@@ -44,10 +44,6 @@ constexpr int kThreads = 64 * kBlocksPerWG;
 constexpr int kTT = 32;                        // tokens per tile (one MFMA group)
 static_assert(kLoaderWave >= kStorerWaves, "the loader issues no stores");
 
-__device__ __forceinline__ uint4 load_row8(const uint16_t* __restrict__ p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
