@@ -240,8 +240,9 @@ batq_status batq_kv_cache_quant(const void* KV_bf16, int64_t T, int64_t HD, int6
 #define BATQ_DECODE_MAX_M 32
 
 /* Workspace bytes batq_w4a4_decode needs for (M, N, K): fp32 partial tiles,
- * one per 256-column chunk, K split and token.  -1 for M outside [0, 32],
- * N < 0 or K not a positive multiple of 256. */
+ * one per 256-column chunk, K split and token.  A split covers one 256-k stage
+ * of K, or two when M > 16 and there are more than 256 (chunk, stage) pairs.
+ * -1 for M outside [0, 32], N < 0 or K not a positive multiple of 256. */
 int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Y[M][N] = deq(Q(X P)) deq(Wp)^T with the activation path fused into the
