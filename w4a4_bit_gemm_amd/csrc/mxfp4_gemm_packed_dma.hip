@@ -171,9 +171,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT]
       const int id = it * 64 + lane_e;
       const int rs = id / (4 * kNT);
       const int cc = id % (4 * kNT);
+      // Lanes 4-7 of every 8 read their upper half first: eight lanes'
+      // 16-byte reads then cover all 32 banks once instead of half of them
+      // twice.
       const float* src = epi + rs * kEpiStride + 8 * cc;
-      const float4 lo = reinterpret_cast<const float4*>(src)[0];
-      const float4 hi = reinterpret_cast<const float4*>(src)[1];
+      const int sw = (cc >> 2) & 1;
+      const float4 first = *reinterpret_cast<const float4*>(src + 4 * sw);
+      const float4 second = *reinterpret_cast<const float4*>(src + 4 - 4 * sw);
+      const float4 lo = sw ? second : first;
+      const float4 hi = sw ? first : second;
       const int64_t row = m0e + 32 * i + rs;
       const int64_t col = c0e + 64 * wave_e + 8 * cc;
       if (row >= p.M || col >= p.N) continue;
@@ -247,15 +253,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     qoff[q] = (uint32_t)gr * krow + 16u * (uint32_t)((lane & 7) ^ swz(row));
   }
   // Activation scales, four stages (32 bytes of a row) per group: wave w
-  // covers rows 32 w + l / 2, 16-byte half l % 2; LDS holds [row][32 bytes].
+  // covers rows 32 w + l % 32, 16-byte half l / 32 (stages 2 h, 2 h + 1), so
+  // LDS holds [wave][half][32 rows][16 bytes].  Rows 16 bytes apart (rather
+  // than 32) put a stage's 64 scale words of a sub-tile on twice as many banks.
   const uint32_t srow = (uint32_t)(p.K >> 5);
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, (short)0, (int)(p.M * (int64_t)srow), 0x00020000);
   uint32_t soff;
   {
-    const int row = 32 * wave + (lane >> 1);
+    const int row = 32 * wave + (lane & 31);
     const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
-    soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane & 1);
+    soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane >> 5);
   }
 #define DMA_A(SLOT, ST)                                                                         \
   _Pragma("unroll") for (int q = 0; q < kQPerWave; ++q)                                         \
@@ -295,14 +303,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   // (behind an empty asm) so that they are not held for every stage at once.
 #define DMA_MMA_STAGE(SLOT, SG, SQI, n)                                                         \
   {                                                                                            \
-    uint32_t so_ = r32 * 32 + 4 * g;                                                           \
+    uint32_t so_ = r32 * 16 + 4 * g;                                                           \
     uint32_t fo0_ = r32 * kRowBytes + 16 * ((4 * g) ^ swz(r32));                                \
     uint32_t fo1_ = r32 * kRowBytes + 16 * ((4 * g + 1) ^ swz(r32));                            \
     uint32_t fo2_ = r32 * kRowBytes + 16 * ((4 * g + 2) ^ swz(r32));                            \
     uint32_t fo3_ = r32 * kRowBytes + 16 * ((4 * g + 3) ^ swz(r32));                            \
     asm volatile("" : "+v"(so_), "+v"(fo0_), "+v"(fo1_), "+v"(fo2_), "+v"(fo3_));              \
     uint32_t sa_[kMT];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 8 * (SQI)); \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 512 * ((SQI) >> 1) + 8 * ((SQI) & 1)); \
     DMA_SUB(SLOT, fo0_, 0, n)                                                                  \
     DMA_SUB(SLOT, fo1_, 1, n)                                                                  \
     DMA_SUB(SLOT, fo2_, 2, n)                                                                  \
@@ -427,9 +435,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, (short)0, (int)(p.M * (int64_t)srow), 0x00020000);
   uint32_t soff;
   {
-    const int row = 32 * wave + (lane >> 1);
+    const int row = 32 * wave + (lane & 31);
     const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
-    soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane & 1);
+    soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane >> 5);
   }
   const uint32_t k16 = 16 * krow;  // 16 rows
 #define DMA_A8(SLOT, ST)                                                                        \
@@ -477,10 +485,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   }
 #define MMA8_STAGE(SLOT, SG, SQI, n)                                                           \
   {                                                                                            \
-    uint32_t so_ = r32 * 32 + 4 * g;                                                           \
+    uint32_t so_ = r32 * 16 + 4 * g;                                                           \
     asm volatile("" : "+v"(so_));                                                              \
     uint32_t sa_[kMT];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 8 * (SQI)); \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 512 * ((SQI) >> 1) + 8 * ((SQI) & 1)); \
     SUB8(SLOT, 0, n)                                                                           \
     SUB8(SLOT, 1, n)                                                                           \
     SUB8(SLOT, 2, n)                                                                           \
