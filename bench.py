@@ -305,7 +305,7 @@ def run_kv(args, torch, w, wl, dev):
                                f"{'MXFP4' if fmt == 4 else 'MXFP8 E4M3'} into permuted slots of a {rows}-row cache",
                    "T": T, "HD": HD, "cache_rows": rows, "fmt": fmt, "buffer_sets": nsets, "clip": not args.no_clip},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": f"transform_quant_kernel<false,{'true' if fmt == 8 else 'false'}>"},
+                     "traffic": None, "kernel": f"kv_cache_quant_kernel<{'true' if fmt == 8 else 'false'}>"},
         "kernels": {"kv_cache_quant": {"us": t_step * 1e6, "GB/s": gbs, "algorithmic_bytes": alg_bytes}},
         "cpu_baseline": None,
     }

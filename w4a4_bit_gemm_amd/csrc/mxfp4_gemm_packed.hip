@@ -499,11 +499,13 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
       const int64_t col = n0 + 8 * cc;
       if (row >= p.M || col >= p.N) continue;
       const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      // Output stores are non-temporal: Y is not read again here, and cached
+      // output lines would evict operand lines that other tiles still reuse.
       if (p.out_f32) {
         float* dst = reinterpret_cast<float*>(p.y) + row * p.N + col;
         if (col + 8 <= p.N && p.vec_store) {
-          reinterpret_cast<float4*>(dst)[0] = lo;
-          reinterpret_cast<float4*>(dst)[1] = hi;
+          __builtin_nontemporal_store(f32x4{lo.x, lo.y, lo.z, lo.w}, reinterpret_cast<f32x4*>(dst));
+          __builtin_nontemporal_store(f32x4{hi.x, hi.y, hi.z, hi.w}, reinterpret_cast<f32x4*>(dst) + 1);
         } else {
           for (int e = 0; e < 8; ++e)
             if (col + e < p.N) dst[e] = v[e];
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
 #pragma unroll
         for (int e = 0; e < 4; ++e) hb[e] = f32x2_to_bf16x2_rne(v[2 * e], v[2 * e + 1]);
         if (col + 8 <= p.N && p.vec_store) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+          __builtin_nontemporal_store(u32x4{hb[0], hb[1], hb[2], hb[3]}, reinterpret_cast<u32x4*>(dst));
         } else {
           for (int e = 0; e < 8; ++e)
             if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));

@@ -107,9 +107,10 @@ struct TQSmem {
 // otherwise one pair per block, read once (activations), which keeps every
 // memory wait out of the activations' tile loop.  F8: MXFP8 (E4M3) codes, one
 // byte per element (the W4A8 setting); otherwise MXFP4 (E2M1), two per byte.
-template <bool PER_ROW, bool F8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
-    TransformQuantArgs p, int64_t gy) {
+// STREAM: non-temporal code and scale stores, for outputs that the next
+// kernel does not read (cache rows written through the slot mapping).
+template <bool PER_ROW, bool F8, bool STREAM>
+__device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& p, int64_t gy) {
   using T = TQSmem<F8>;
   constexpr int kRing = T::kRing;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kRing * T::kX];
@@ -210,9 +211,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int64_t tok = tok0 + row;
       if (tok < p.rows && c / (kChunks / 8) < nblk) {
         const int64_t orow = out_row(tok);
-        if (orow >= 0)
-          *reinterpret_cast<uint4*>(p.q + orow * qld + blk0 * (2 * kChunks) + 16 * c) =
-              *reinterpret_cast<const uint4*>(qsb + row * T::kQRow + 16 * c);
+        if (orow >= 0) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qsb + row * T::kQRow + 16 * c);
+          u32x4* dst = reinterpret_cast<u32x4*>(p.q + orow * qld + blk0 * (2 * kChunks) + 16 * c);
+          if constexpr (STREAM) __builtin_nontemporal_store(v, dst);
+          else *dst = v;
+        }
       }
     }
     if (lane < 8) {
@@ -223,7 +227,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         uint8_t* dst = p.s + orow * nb + blk0;
         const uint8_t* src = ss + sb * kTT * 8 + row * 8;
         if (nblk == 8 && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+          const unsigned long long v = *reinterpret_cast<const unsigned long long*>(src);
+          if constexpr (STREAM) __builtin_nontemporal_store(v, reinterpret_cast<unsigned long long*>(dst));
+          else *reinterpret_cast<unsigned long long*>(dst) = v;
         } else {
           for (int c = 0; c < nblk; ++c) dst[c] = src[c];
         }
@@ -281,6 +287,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
+template <bool PER_ROW, bool F8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
+    TransformQuantArgs p, int64_t gy) {
+  transform_quant_tiles<PER_ROW, F8, false>(p, gy);
+}
+
+// Cache rows are not read by the next kernel, so they are streamed past L2.
+template <bool F8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kv_cache_quant_kernel(
+    TransformQuantArgs p, int64_t gy) {
+  transform_quant_tiles<false, F8, true>(p, gy);
+}
+
 }  // namespace
 
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream) {
@@ -305,7 +324,12 @@ hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t st
   if (gy > tiles) gy = tiles;
   const dim3 grid((unsigned)(gx * gy));
   const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
-  if (args.fp8) {
+  if (args.slot != nullptr && !per_row) {
+    if (args.fp8)
+      hipLaunchKernelGGL((kv_cache_quant_kernel<true>), grid, dim3(kThreads), 0, stream, args, gy);
+    else
+      hipLaunchKernelGGL((kv_cache_quant_kernel<false>), grid, dim3(kThreads), 0, stream, args, gy);
+  } else if (args.fp8) {
     if (per_row)
       hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args, gy);
     else
