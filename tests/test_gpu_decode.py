@@ -127,6 +127,31 @@ def test_decode_deterministic_and_reusable_workspace(w):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+def test_decode_workspace_reused_across_shapes(w):
+    """One workspace, sized for the largest call and filled with junk, serves
+    calls of different M, N and K in turn (each call's partial area overlaps
+    the earlier calls' data); each matches a call on a fresh workspace bit for
+    bit."""
+    note("case: decode workspace reuse across shapes")
+    rng = np.random.default_rng(7)
+    shapes = [(32, 12288, 4096), (3, 300, 512), (16, 4096, 12288), (1, 8192, 256), (32, 12288, 4096)]
+    big = max(w.decode_workspace_bytes(M, N, K) for M, N, K in shapes)
+    ws = torch.full((big,), 0x5A, dtype=torch.uint8, device=DEV)
+    for M, N, K in shapes:
+        note(f"  shape M={M} N={N} K={K}")
+        Wq = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).to(DEV)
+        Ws = torch.from_numpy(rng.integers(118, 124, (N, K // 32), dtype=np.uint8)).to(DEV)
+        Wp = w.weight_pack(Wq, Ws)
+        X = dev_bf16(np.ascontiguousarray(
+            (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)))
+        A = dev_f32(np.eye(8, dtype=np.float32) + 0.05 * rng.standard_normal((8, 8)).astype(np.float32))
+        B = dev_f32(np.tile(np.eye(4, dtype=np.float32), (K // 32, 1, 1)))
+        ref = w.w4a4_decode(X, A, B, None, None, Wp, w.decode_workspace(M, N, K, DEV), out_dtype=torch.float32)
+        got = w.w4a4_decode(X, A, B, None, None, Wp, ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int32), got.view(torch.int32))
+
+
 @pytest.mark.parametrize("cfg", [1, 4])
 def test_decode_end_to_end(w, cfg):
     """The chain X, W -> Y in one fused launch against the oracle chain (config
