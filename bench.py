@@ -297,6 +297,7 @@ def run_kv(args, torch, w, wl, dev):
     t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
     alg_bytes = T * HD * 2 + T * (qcols + HD // 32) + T * 8  # rows read, codes + scales written, slots read
     gbs = alg_bytes / t_step / 1e9
+    kv_kernel = f"kv_cache_quant_kernel<{'true' if fmt == 8 else 'false'}>"
     out = {
         "metric": METRIC_KV, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -305,7 +306,8 @@ def run_kv(args, torch, w, wl, dev):
                                f"{'MXFP4' if fmt == 4 else 'MXFP8 E4M3'} into permuted slots of a {rows}-row cache",
                    "T": T, "HD": HD, "cache_rows": rows, "fmt": fmt, "buffer_sets": nsets, "clip": not args.no_clip},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": f"kv_cache_quant_kernel<{'true' if fmt == 8 else 'false'}>"},
+                     "traffic": load_traffic("transform_quant.hip", kv_kernel, f"kv{fmt}_{T}x{HD}"),
+                     "kernel": kv_kernel},
         "kernels": {"kv_cache_quant": {"us": t_step * 1e6, "GB/s": gbs, "algorithmic_bytes": alg_bytes}},
         "cpu_baseline": None,
     }
