@@ -442,22 +442,22 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # Per-kernel mean launch duration: `steps` back-to-back launches of one
-    # kernel over the same rotating buffers, between two HIP events recorded on
-    # the stream the kernels are launched on (torch's current stream).  One
-    # event pair per batch, so the events add no gap between launches.
-    def batch_seconds(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(args.steps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / args.steps
-
-    t_act = np.array([batch_seconds(act)])
-    t_gemm = np.array([batch_seconds(gemm)])
+    # Per-kernel launch durations inside the step: a second pass over the same
+    # `steps` steps with a HIP event before the transform, one between the two
+    # kernels and one after the GEMM, all recorded on the stream the kernels
+    # are launched on (torch's current stream).  The events stay out of the
+    # timed region above.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[3 * i].record()
+        act(i)
+        evs[3 * i + 1].record()
+        gemm(i)
+        evs[3 * i + 2].record()
+    torch.cuda.synchronize()
+    t_act = np.array([evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)]) * 1e-3
+    t_gemm = np.array([evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(args.steps)]) * 1e-3
 
     flops = 2.0 * M * N * K
     act_bytes = M * K * 2 + M * xq_row + M * K // 32  # algorithmic: read bf16, write codes + scales
