@@ -41,6 +41,9 @@ constexpr int kBlocksPerWG = 8;  // one 32-channel block per compute wave; 8 blo
 constexpr int kLoaderWave = kBlocksPerWG - 1;  // also issues the global -> LDS tile loads
 constexpr int kStorerWaves = 4;                // waves 0-3 also write the staged codes and scales
 constexpr int kThreads = 64 * kBlocksPerWG;
+// Cache policy of the X loads: non-temporal (bit 1 of the buffer instructions'
+// cache-policy field), since every X byte is read once.
+constexpr int kStreamLoad = 2;
 constexpr int kTT = 32;                        // tokens per tile (one MFMA group)
 static_assert(kLoaderWave >= kStorerWaves, "the loader issues no stores");
 
@@ -166,7 +169,7 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
 #pragma unroll
     for (int q = 0; q < kTT / 2; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + q * 1024), 16, (int)voff[q & 7],
-                                               (int)((q >> 3) * 16 * ld2), 0, 0);
+                                               (int)((q >> 3) * 16 * ld2), 0, kStreamLoad);
   };
   // The first tiles are requested before anything else, so that their latency
   // overlaps the factor and ratio loads below (loads issued after them only
