@@ -39,6 +39,15 @@ __device__ __forceinline__ f32x16 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32
 }
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+// Weight records are read once per step: non-temporal loads keep them from
+// displacing the partial tiles that the reduction reads next.
+__device__ __forceinline__ uint4 ld16_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld4_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 
 // Inputs of one activation block for the wave's 32 token slots: factor
 // entries, the lane's 16 channels of token j (zero for j >= M), the ratios.
@@ -103,11 +112,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int n
       const uint8_t* r1 = p.wp + (g1 * nst + s0 + t) * kPackGroupBytes + 16 * lane;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        b0[t][jj] = ld16(r0 + 1024 * jj);
-        b1[t][jj] = ld16(r1 + 1024 * jj);
+        b0[t][jj] = ld16_stream(r0 + 1024 * jj);
+        b1[t][jj] = ld16_stream(r1 + 1024 * jj);
       }
-      bs0[t] = ld4(r0 + 4096 - 12 * lane);
-      bs1[t] = ld4(r1 + 4096 - 12 * lane);
+      bs0[t] = ld4_stream(r0 + 4096 - 12 * lane);
+      bs1[t] = ld4_stream(r1 + 4096 - 12 * lane);
     }
   }
 
