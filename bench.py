@@ -2,16 +2,24 @@
 
 One step = the whole online path for one batch: the fused activation block
 transform + clip + MXFP4 quantisation kernel followed by the W4A4 MXFP4 GEMM
-(bf16 output).  The weight side (P^-1 W^T, clip, quantise) is offline and runs
-once before timing.  Default workload: the up/gate projection prefill layer,
-X 2048 x 4096 bf16 and W 12288 x 4096 bf16, shared factor 8x8 / private 4x4.
+(bf16 output).  The weight side (P^-1 W^T, clip, quantise, pack) is offline
+and runs once before timing.  Default workload: the large-prefill layer (batch
+64 x prefill 256 = 16384 tokens), X 16384 x 4096 bf16 and W 4096 x 4096 bf16,
+shared factor 8x8 / private 4x4; ``--config 2`` is the up/gate projection
+(2048 x 4096 x 12288), ``--config 5 --a N`` a point of the shared-factor sweep.
 
 Inputs are resident in HBM when timing starts.  Steps rotate through several
 copies of every buffer (more bytes than the 256 MB Infinity Cache) so a step
 cannot be served from the cache a previous step filled.
 
 Prints ONE JSON line.  ``value`` is the step throughput in TFLOP/s of W4A4 GEMM
-work (2 M N K per step) including the activation kernel's time.
+work (2 M N K per step) including the activation kernel's time.  Per-kernel
+durations come from loops of that kernel alone over the same buffers, timed
+with HIP events on the launch stream at the loops' ends only (an event between
+the two kernels of a step adds its own gap to both), and the line checks that
+they add up inside the step.  ``--ceiling`` runs only the ceiling probes (the
+FP4 matrix instruction in a register loop with the shader clock it sustains,
+HBM read and copy streams).
 """
 from __future__ import annotations
 
@@ -44,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--a", type=int, default=8, help="shared factor size (config 5 sweep)")
     ap.add_argument("--factors", choices=["gpk", "hadamard"], default="gpk",
                     help="transform factors: seeded near-identity GPK, or the block-Hadamard rotation (BRQ)")
@@ -62,6 +70,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="run only the ceiling probes (FP4 MFMA loop and shader clock, HBM read and copy)")
+    ap.add_argument("--no-ceiling", action="store_true", help="leave the ceiling probes out of the bench line")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="minimum oracle time for the CPU baseline")
     return ap.parse_args()
@@ -106,40 +117,75 @@ def load_traffic(kernel_file: str, kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(wl, min_seconds: float, fmt: str = "e2m1"):
-    """The oracle, as it stands, on the same workload: the whole step (every
-    token row through the activation path, then the full GEMM against every
-    prepared weight row), repeated until ``min_seconds`` have passed."""
+def _blas_threads() -> int:
     import threadpoolctl
 
+    return int(max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] or [1]))
+
+
+def scalar_oracle_tiny():
+    """The pure-Python loop oracle, single-threaded, on the tiny config:
+    activations (64 x 256), weights (256 x 256) and the exact rational GEMM of
+    the first 16 token rows; seconds each."""
+    from oracle import scalar as osc
+    from workloads import gen
+
+    wl = gen.make_workload(1)
+    t0 = time.perf_counter()
+    xc, xs = osc.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
+    t1 = time.perf_counter()
+    wc, ws = osc.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha, wl.wbeta)
+    t2 = time.perf_counter()
+    osc.gemm_exact(xc[:16], xs[:16], wc, ws)
+    t3 = time.perf_counter()
+    return {"act_s": t1 - t0, "weight_prep_s": t2 - t1, "gemm_exact_16_rows_s": t3 - t2,
+            "act_GBs": wl.M * wl.K * (2 + 0.5 + 1 / 32) / (t1 - t0) / 1e9,
+            "gemm_exact_GFLOPs": 2.0 * 16 * wl.N * wl.K / (t3 - t2) / 1e9, "threads": 1}
+
+
+def cpu_baseline(wl, min_seconds: float, fmt: str = "e2m1", max_rows: int = 1024):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    first ``max_rows`` token rows (every row of a smaller config) through the
+    activation path, then their GEMM against every prepared weight row,
+    repeated until ``min_seconds`` have passed, scaled to the step's TFLOP/s.
+    Beside it: the oracle's offline weight preparation of the whole weight
+    (once) and the single-threaded loop oracle on the tiny config."""
     from oracle import batquant as ob
 
-    wprep = ob.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha, wl.wbeta)  # offline, untimed
+    rows = min(wl.M, max_rows)
+    t0 = time.perf_counter()
+    wprep = ob.weight_prep(wl.W_bits, wl.A, wl.B, wl.walpha, wl.wbeta)  # offline, timed once
+    t_wprep = time.perf_counter() - t0
+    xb = wl.X_bits[:rows]
     reps, t_act, t_gemm = 0, 0.0, 0.0
-    while reps == 0 or (t_act + t_gemm < min_seconds and reps < 8):
+    while reps == 0 or (t_act + t_gemm < min_seconds and reps < 64):
         t0 = time.perf_counter()
-        x = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta, fmt=fmt)
+        x = ob.act_transform_quant(xb, wl.A, wl.B, wl.alpha, wl.beta, fmt=fmt)
         t1 = time.perf_counter()
         ob.gemm(x.codes, x.scales, wprep.codes, wprep.scales, x_fmt=fmt)
         t2 = time.perf_counter()
         t_act += t1 - t0
         t_gemm += t2 - t1
         reps += 1
-    flops = 2.0 * wl.M * wl.N * wl.K
-    info = threadpoolctl.threadpool_info()
-    blas_threads = max([d.get("num_threads", 1) for d in info] or [1])
+    flops = 2.0 * rows * wl.N * wl.K
+    threads = _blas_threads()
+    scal = scalar_oracle_tiny()
+    wbytes = wl.N * wl.K * (2 + 0.5 + 1 / 32)
     return {
         "value": flops * reps / (t_act + t_gemm) / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"the full step ({wl.M} token rows through the fp64 oracle activation path, then the "
-                   f"{wl.M}x{wl.N}x{wl.K} dequantised fp64 GEMM), {reps} repetition(s): activation "
-                   f"{t_act / reps:.2f} s, GEMM {t_gemm / reps:.2f} s per step; weight preparation offline "
-                   f"and untimed; BLAS threads {blas_threads}, host cores visible "
-                   f"{len(os.sched_getaffinity(0))}"),
+        "sample": (f"{rows} of the {wl.M} token rows through the fp64 oracle activation path, then their "
+                   f"{rows}x{wl.N}x{wl.K} dequantised fp64 GEMM, {reps} repetition(s): activation "
+                   f"{t_act / reps:.2f} s, GEMM {t_gemm / reps:.2f} s each; BLAS threads {threads}, host cores "
+                   f"visible {len(os.sched_getaffinity(0))}; also timed: the oracle's weight preparation of the "
+                   f"whole {wl.N}x{wl.K} weight (once) and the single-threaded loop oracle on the tiny config"),
         "seconds_measured": t_act + t_gemm,
-        "steps_per_second": reps / (t_act + t_gemm),
+        "act_GBs": rows * wl.K * (2 + 0.5 + 1 / 32) * reps / t_act / 1e9,
+        "gemm_TFLOPs": flops * reps / t_gemm / 1e12,
+        "weight_prep": {"s": t_wprep, "GBs": wbytes / t_wprep / 1e9, "rows": wl.N},
+        "scalar_tiny": scal,
     }
 
 
@@ -246,7 +292,9 @@ def run_decode(args, torch, w, wl, dev):
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_min_seconds)
-        cb["value"] = alg_bytes * cb["steps_per_second"] / 1e9
+        # the oracle's rate over the same bytes per step (its sample covers every token row here)
+        step_s = 2.0 * wl.M * wl.N * wl.K / (cb["value"] * 1e12)
+        cb["value"] = alg_bytes / step_s / 1e9
         cb["unit"] = "GB/s"
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
@@ -320,10 +368,7 @@ def run_kv(args, torch, w, wl, dev):
                               None if args.no_clip else kv.beta, fmt="e2m1" if fmt == 4 else "e4m3")
             reps += 1
         dt = (time.perf_counter() - t_start) / reps
-        import threadpoolctl
-
-        cores = max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] or [1])
-        out["cpu_baseline"] = {"value": alg_bytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+        out["cpu_baseline"] = {"value": alg_bytes / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
                                "sample": f"the full write ({T} rows through the fp64 oracle path), {reps} repetition(s), "
                                          f"{dt:.2f} s each"}
     print(json.dumps(out), flush=True)
@@ -348,6 +393,66 @@ def calibrate_copy(torch, dev, steps):
                       "launches": 2 * steps, "GB/s": 8 * n / dt / 1e9}), flush=True)
 
 
+def measure_ceilings(torch, w, dev):
+    """The ceilings the kernels are set against, measured on this GPU: the
+    block-scaled FP4 MFMA in a register-only loop (random and constant operand
+    bits, 2 and 1 waves per SIMD) with the shader clock it ran at, and HBM
+    read and copy streams over buffers eight times the Infinity Cache."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    mf = {}
+    iters = 20000
+    for name, data, per_cu in (("random_2w", 1, 2), ("const_2w", 0, 2), ("random_1w", 1, 1)):
+        wgs = cus * per_cu
+        sink = torch.empty(4 * wgs, dtype=torch.float32, device=dev)
+        clocks = torch.zeros(8 * wgs, dtype=torch.int64, device=dev)
+        for _ in range(2):
+            w.probe_mfma_fp4(wgs, iters, data, 7, sink, clocks)
+        reps = 4
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            w.probe_mfma_fp4(wgs, iters, data, 7, sink, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) * 1e-3 / reps
+        flops = 4.0 * wgs * iters * 8 * 2 * 32 * 32 * 64
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        mf[f"{name}_TFLOPs"] = flops / dt / 1e12
+        # shader-clock cycles per 100 MHz real-time tick, over every wave of the last launch
+        mf[f"{name}_clock_MHz"] = float(c[:, 0].sum() / c[:, 1].sum() * 100.0)
+    gran = w.probe_stream_granule()
+    nbytes = 32 * gran  # 2 GiB
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    rsink = torch.empty(2048, dtype=torch.int32, device=dev)
+    csrc = src[: nbytes // 8]
+    cdst = torch.empty(nbytes // 8, dtype=torch.int32, device=dev)
+
+    def stream(fn, nb, reps=5):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return nb * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    read = stream(lambda: w.probe_hbm_read(src, rsink), nbytes)
+    copy = stream(lambda: w.probe_hbm_copy(csrc, cdst), 2 * (nbytes // 2))
+    del src, cdst
+    return {"mfma_fp4_loop": mf, "hbm_read_GBs": read, "hbm_copy_GBs": copy,
+            "note": "FP4 32x32x64 block-scaled MFMA, 8 independent chains per wave, no memory traffic; clock = "
+                    "s_memtime cycles per s_memrealtime tick x 100 MHz; HBM read of 2 GiB, copy of 1 GiB -> 1 GiB"}
+
+
+def run_ceilings(args, torch, w, dev):
+    ceil = measure_ceilings(torch, w, dev)
+    print(json.dumps({"ceilings": ceil, "published": {"mfma_fp4_TFLOPs": MXFP4_PEAK_TFLOPS,
+                                                     "hbm_GBs": HBM_PEAK_GBS}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -368,6 +473,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
         calibrate_copy(torch, dev, args.steps)
+        return
+    if args.ceiling:
+        run_ceilings(args, torch, w, dev)
         return
     wl = gen.make_workload(args.config, a=args.a)
     M, K, N = wl.M, wl.K, wl.N
@@ -434,48 +542,52 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps between two synchronisations
+    # timed region: exactly `steps` steps between two synchronisations; HIP
+    # events on the launch stream (torch's current stream) at its two ends
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
         step(i)
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    t_step = ev0.elapsed_time(ev1) * 1e-3 / args.steps
 
-    # Per-kernel launch durations inside the step: a second pass over the same
-    # `steps` steps with a HIP event before the transform, one between the two
-    # kernels and one after the GEMM, all recorded on the stream the kernels
-    # are launched on (torch's current stream).  The events stay out of the
-    # timed region above.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        evs[3 * i].record()
-        act(i)
-        evs[3 * i + 1].record()
-        gemm(i)
-        evs[3 * i + 2].record()
-    torch.cuda.synchronize()
-    t_act = np.array([evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)]) * 1e-3
-    t_gemm = np.array([evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(args.steps)]) * 1e-3
+    # Per-kernel launch durations: each kernel alone, `steps` launches over the
+    # same rotating buffers, events at the loop's two ends only (an event
+    # between the two kernels of a step would add its own gap to both).
+    def loop_seconds(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / args.steps
+
+    t_act = loop_seconds(act)
+    t_gemm = loop_seconds(gemm)
 
     flops = 2.0 * M * N * K
     act_bytes = M * K * 2 + M * xq_row + M * K // 32  # algorithmic: read bf16, write codes + scales
     gemm_bytes = M * xq_row + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
     mma_peak = FP8_PEAK_TFLOPS if fp8 else MXFP4_PEAK_TFLOPS
-    act_gbs = act_bytes / t_act.mean() / 1e9
-    gemm_tflops = flops / t_gemm.mean() / 1e12
+    act_gbs = act_bytes / t_act / 1e9
+    gemm_tflops = flops / t_gemm / 1e12
     ai = flops / gemm_bytes
     gemm_hbm_bound = ai < mma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if gemm_hbm_bound:
-        gemm_roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm.mean() / 1e9, "peak": HBM_PEAK_GBS,
+        gemm_roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s"}
     else:
         gemm_roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": mma_peak, "unit": "TFLOP/s"}
     gemm_roof["frac"] = gemm_roof["achieved"] / gemm_roof["peak"]
     act_roof = {"bound": "hbm", "achieved": act_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": act_gbs / HBM_PEAK_GBS}
-    dominant_is_gemm = t_gemm.mean() >= t_act.mean()
+    dominant_is_gemm = t_gemm >= t_act
     roof = dict(gemm_roof if dominant_is_gemm else act_roof)
     nst = K // 256
     gs = "true" if nst % 4 == 0 else "false"
@@ -519,15 +631,23 @@ def main():
         },
         "roofline": roof,
         "kernels": {
-            "transform_quant": {"us": float(t_act.mean() * 1e6), "GB/s": act_gbs,
+            "transform_quant": {"us": t_act * 1e6, "GB/s": act_gbs,
                                 "frac_hbm": act_gbs / HBM_PEAK_GBS, "algorithmic_bytes": act_bytes,
                                 "roofline": act_roof},
-            "gemm": {"kernel": gemm_kernel, "us": float(t_gemm.mean() * 1e6), "TFLOP/s": gemm_tflops,
+            "gemm": {"kernel": gemm_kernel, "us": t_gemm * 1e6, "TFLOP/s": gemm_tflops,
                      "frac_mfma": gemm_tflops / mma_peak, "flops": flops,
                      "operand_output_bytes": gemm_bytes, "roofline": gemm_roof},
         },
+        "step": {"gpu_us": t_step * 1e6, "kernels_sum_us": (t_act + t_gemm) * 1e6,
+                 "kernels_sum_over_step": (t_act + t_gemm) / t_step,
+                 "timing": "step: events around the timed steps; kernels: events around a loop of each kernel alone"},
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        ceil = measure_ceilings(torch, w, dev)
+        out["ceilings"] = ceil
+        out["kernels"]["gemm"]["frac_of_mfma_loop"] = gemm_tflops / ceil["mfma_fp4_loop"]["random_2w_TFLOPs"]
+        out["kernels"]["transform_quant"]["frac_of_hbm_read"] = act_gbs / ceil["hbm_read_GBs"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds, "e4m3" if fp8 else "e2m1")
     print(json.dumps(out), flush=True)

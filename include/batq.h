@@ -175,8 +175,8 @@ int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8
 
 /* ------------------------------------------------ W4A8: MXFP8 activations
  * The pages also report a W4A8 setting: MXFP8 activations against the same
- * MXFP4 weights [nubint.ai review, Table 2; en.papernotes.org, Experiments].
- * MXFP8 here is the OCP MX E4M3 format: one code byte per element (sign,
+ * MXFP4 weights [nubint.ai review, Table 2], with E4M3 elements
+ * [en.papernotes.org, Loss & Training].  The encoding is the OCP MX E4M3 format: one code byte per element (sign,
  * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest value
  * 448, S.1111.111 never produced), one UE8M0 scale per 32 elements with
  * exponent floor(log2 amax) - 8 clamped to [-127, 127], elements rounded to

@@ -106,10 +106,11 @@ def shared_exponent(amax: np.ndarray, emax: int = E2M1_MAX_EXP) -> np.ndarray:
 # MXFP8 (E4M3) elements, for the W4A8 setting of the pages
 # ---------------------------------------------------------------------------
 # The pages report a W4A8 configuration (MXFP8 activations with MXFP4 weights)
-# [nubint.ai review, Table 2; en.papernotes.org, Experiments] without defining
-# the element format; it is the OCP MX v1.0 E4M3 format: sign, 4 exponent bits
-# (bias 7), 3 mantissa bits, subnormals at exponent field 0, no infinities,
-# S.1111.111 is NaN, largest finite value 448 = 1.75 * 2**8.
+# [nubint.ai review, Table 2] and name E4M3 as its element format
+# [en.papernotes.org, Loss & Training].  The bit-level definition is the OCP
+# MX v1.0 E4M3 format: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+# subnormals at exponent field 0, no infinities, S.1111.111 is NaN, largest
+# finite value 448 = 1.75 * 2**8.
 
 E4M3_MAX_EXP = 8
 E4M3_MAX = 448.0

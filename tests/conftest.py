@@ -15,3 +15,26 @@ def pytest_configure(config):
 
 def golden_path(name: str) -> str:
     return os.path.join(ROOT, "tests", "golden", name)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Per-comparison parity counts (codes and scales against the oracle), so
+    that they stay in the output of every run, not only under -s."""
+    from tests import parity
+
+    if not parity.RESULTS:
+        return
+    tr = terminalreporter
+    tr.section("parity counts (codes/scales vs oracle)")
+    tr.write_line(f"{'comparison':44s} {'elements':>11s} {'mism':>5s} {'out-1e-6':>8s} {'1e-6 set':>8s} "
+                  f"{'free':>6s} {'free blk':>8s} {'mism/elem':>9s}")
+    for r in parity.RESULTS:
+        tr.write_line(f"{r['label'][:44]:44s} {r['elements']:11d} {r['mismatches']:5d} "
+                      f"{r['mismatches_outside_literal']:8d} {r['literal_exempt']:8d} {r['free']:6d} "
+                      f"{r['free_blocks']:8d} {r['mismatches'] / r['elements']:9.1e}")
+    out = os.path.join(ROOT, "gpurun_out")
+    if os.path.isdir(out):
+        import json
+
+        with open(os.path.join(out, "parity_counts.json"), "w") as f:
+            json.dump(parity.RESULTS, f, indent=1)

@@ -1,6 +1,8 @@
 """Comparison helpers for the GPU parity tests (HIP path vs oracle)."""
 from __future__ import annotations
 
+from typing import Optional
+
 import numpy as np
 
 from oracle import batquant as ob
@@ -17,21 +19,71 @@ def rank(codes: np.ndarray, fmt: str = "e2m1") -> np.ndarray:
     return np.where(c & sign, -mag - 1, mag)
 
 
+#: Every comparison made by compare_quant, for the end-of-session summary
+#: (tests/conftest.py prints it, so the counts stay in the test output).
+RESULTS = []
+
+#: Rounding boundaries of E2M1 magnitudes: the midpoints of the grid.
+E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def _midpoints(fmt: str) -> np.ndarray:
+    if fmt == "e2m1":
+        return E2M1_MIDPOINTS
+    g = ob.E4M3_GRID
+    return (g[1:] + g[:-1]) / 2.0
+
+
+def literal_window(dec: ob.Decisions, fmt: str = "e2m1", rel: float = 1e-6) -> np.ndarray:
+    """The exempt set as the stated parity rule words it: elements whose value
+    (clipped, divided by the block scale) lies within ``rel`` relative of a
+    rounding boundary of the element format.  Scales get no exemption.
+    Returns a bool mask [rows, K]."""
+    rows, K = dec.codes.shape
+    z = dec.z32.astype(np.float64).reshape(rows, K // ob.BLOCK, ob.BLOCK)
+    e = dec.scales.astype(np.int64) - 127
+    v = np.abs(np.ldexp(z, -e[..., None])).reshape(rows, K)
+    mids = _midpoints(fmt)
+    i = np.clip(np.searchsorted(mids, v), 1, len(mids) - 1)
+    d = np.minimum(np.abs(v - mids[i - 1]) / mids[i - 1], np.abs(v - mids[i]) / mids[i])
+    return d <= rel
+
+
 def compare_quant(packed_gpu: np.ndarray, scales_gpu: np.ndarray, dec: ob.Decisions, *, max_frac: float = 1e-5,
-                  label: str = "", fmt: str = "e2m1") -> dict:
-    """Scales bit-exact outside free blocks; codes bit-exact outside the free set
-    (free elements and the codes of free blocks), exact zeros may carry either
-    sign; every mismatch at a free element is to an adjacent code; mismatches
-    are fewer than ``max_frac`` of the elements on large inputs."""
+                  label: str = "", fmt: str = "e2m1", literal: Optional[bool] = None) -> dict:
+    """The parity rule for MX codes and scales (GPU against the oracle's
+    decisions on the same input).
+
+    * Scales: bit-exact, every block.
+    * Codes: bit-exact except where the two may legitimately differ.  A code
+      mismatch must (a) lie in the oracle's free set (the element's, or its
+      block's, decision flips inside the rigorous fp32 error window of the
+      transform, gamma_36 sum |x||P|), (b) land on an adjacent code, and,
+      with ``literal``, (c) lie in the stated exempt set (within 1e-6
+      relative of a rounding boundary: ``literal_window``).  Exact zeros may
+      carry either sign.
+    * Mismatches are fewer than ``max_frac`` of the elements (on small inputs
+      that means none); with ``literal``, on 100k elements or more, the
+      stated exempt set is also fewer than ``max_frac`` of them.
+    ``literal`` defaults to on for E2M1 codes, the format the stated rule
+    names.  E4M3 codes (the W4A8 activations) have 126 rounding boundaries
+    per binade pattern instead of 7, so the 1e-6 window holds a few 1e-5 of
+    the elements and fp32 flips land outside it; they are held to (a), (b)
+    and the mismatch cap.
+    Returns the counts and records them in ``RESULTS``."""
+    if literal is None:
+        literal = fmt == "e2m1"
     codes_gpu = ob.unpack_codes(packed_gpu) if fmt == "e2m1" else np.asarray(packed_gpu, np.uint8)
     mask = 7 if fmt == "e2m1" else 0x7F
     assert codes_gpu.shape == dec.codes.shape, label
     assert scales_gpu.shape == dec.scales.shape, label
     rows, K = dec.codes.shape
-    blk_free_el = np.repeat(dec.block_free, 32, axis=1)
-    bad_scale = (scales_gpu != dec.scales) & ~dec.block_free
-    assert not bad_scale.any(), f"{label}: {int(bad_scale.sum())} scale mismatches outside free blocks, " \
+    n = rows * K
+    bad_scale = scales_gpu != dec.scales
+    assert not bad_scale.any(), f"{label}: {int(bad_scale.sum())} scale mismatches " \
+                                f"({int((bad_scale & dec.block_free).sum())} in free blocks), " \
                                 f"first at {np.argwhere(bad_scale)[0].tolist()}"
+    blk_free_el = np.repeat(dec.block_free, ob.BLOCK, axis=1)
     mism = codes_gpu != dec.codes
     zero_ok = dec.zero_sign_free & ((codes_gpu & mask) == 0) & ((dec.codes & mask) == 0)
     mism &= ~zero_ok
@@ -41,15 +93,21 @@ def compare_quant(packed_gpu: np.ndarray, scales_gpu: np.ndarray, dec: ob.Decisi
         raise AssertionError(f"{label}: {int(hard.sum())} code mismatches outside the free set; first at row {m} "
                              f"col {k}: gpu {codes_gpu[m, k]} oracle {dec.codes[m, k]} y64 {dec.y64[m, k]!r} "
                              f"scale {dec.scales[m, k // 32]}")
-    soft = mism & dec.elem_free & ~blk_free_el
-    if soft.any():
-        assert np.all(np.abs(rank(codes_gpu[soft], fmt) - rank(dec.codes[soft], fmt)) <= 1), label
+    if mism.any():
+        assert np.all(np.abs(rank(codes_gpu[mism], fmt) - rank(dec.codes[mism], fmt)) <= 1), \
+            f"{label}: a mismatch is not to an adjacent code"
+    lit = literal_window(dec, fmt)
     n_mism = int(mism.sum())
-    n = rows * K
-    if n >= 100_000:
-        assert n_mism < max_frac * n, f"{label}: {n_mism} mismatches of {n}"
-    return {"elements": n, "mismatches": n_mism, "free": dec.n_exempt,
-            "free_blocks": int(dec.block_free.sum())}
+    n_outside_literal = int((mism & ~lit).sum())
+    st = {"label": label, "elements": n, "mismatches": n_mism, "mismatches_outside_literal": n_outside_literal,
+          "literal_exempt": int(lit.sum()), "free": dec.n_exempt, "free_blocks": int(dec.block_free.sum())}
+    RESULTS.append(st)
+    assert n_mism < max_frac * n or n_mism == 0, f"{label}: {n_mism} mismatches of {n}"
+    if literal:
+        assert n_outside_literal == 0, f"{label}: {n_outside_literal} mismatches outside the stated 1e-6 window"
+    if literal and n >= 100_000:
+        assert st["literal_exempt"] < max_frac * n, f"{label}: stated exempt set {st['literal_exempt']} of {n}"
+    return st
 
 
 def gemm_bound(abs_sum: np.ndarray, K: int) -> np.ndarray:

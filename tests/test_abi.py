@@ -24,10 +24,15 @@ def lib():
     return binding._load()
 
 
-def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(batq_[a-z0-9_]+)\s*\(", src)))
+PROBE_HEADER = os.path.join(ROOT, "include", "batq_probe.h")
+
+
+def declared_functions(headers=(HEADER, PROBE_HEADER)):
+    names = set()
+    for h in headers:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(batq_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -36,7 +41,8 @@ def test_header_declares_the_entry_points():
               "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
               "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
               "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode",
-              "batq_kv_cache_quant", "batq_packed_gemm_kernel"):
+              "batq_kv_cache_quant", "batq_packed_gemm_kernel", "batq_probe_mfma_fp4", "batq_probe_hbm_read",
+              "batq_probe_hbm_copy", "batq_probe_stream_granule"):
         assert n in names
 
 
@@ -252,3 +258,18 @@ def test_gpk_invert_rejects_singular(lib):
     assert st == SINGULAR
     assert lib.batq_gpk_invert(8, 8, 2, A.ctypes.data, B.ctypes.data, out_a.ctypes.data,
                                out_b.ctypes.data) == SHAPE
+
+
+def test_probe_argument_checks(lib):
+    g = lib.batq_probe_stream_granule()
+    assert g == 2048 * 256 * 8 * 16
+    assert lib.batq_probe_mfma_fp4(0, 10, 1, 7, FAKE, FAKE, None) == SHAPE
+    assert lib.batq_probe_mfma_fp4(4, 0, 1, 7, FAKE, FAKE, None) == SHAPE
+    assert lib.batq_probe_mfma_fp4(4, 10, 1, 7, 0, FAKE, None) == NULL
+    assert lib.batq_probe_mfma_fp4(4, 10, 1, 7, FAKE, FAKE + 4, None) == ALIGN
+    assert lib.batq_probe_hbm_read(FAKE, g + 16, FAKE, None) == SHAPE
+    assert lib.batq_probe_hbm_read(0, g, FAKE, None) == NULL
+    assert lib.batq_probe_hbm_read(FAKE + 8, g, FAKE, None) == ALIGN
+    assert lib.batq_probe_hbm_copy(FAKE, FAKE, 0, None) == SHAPE
+    assert lib.batq_probe_hbm_copy(FAKE, 0, g, None) == NULL
+    assert lib.batq_probe_hbm_copy(FAKE, FAKE + 4, g, None) == ALIGN

@@ -234,6 +234,20 @@ def test_weight_prep_tiny(w, clip):
     parity.compare_quant(q, s, dec, label=f"weight tiny clip={clip}")
 
 
+@pytest.mark.parametrize("a", [a for a in gen.SWEEP_A])
+def test_weight_prep_shared_factor_sweep(w, a):
+    """The offline weight side (the per-row-ratio instance of the transform
+    kernel) for every shared-factor size of the sweep, on the config 5 weight
+    (4096 x 4096): sampled rows, every code and scale against the oracle."""
+    note(f"case: weight prep sweep a={a} (config 5 weight)")
+    wl = gen.make_workload(5, a=a)
+    q, s = run_weight(w, wl)
+    rows = _sample_rows(wl.N, 256, 40 + a)
+    dec = ob.weight_prep(wl.W_bits[rows], wl.A, wl.B, wl.walpha[rows], wl.wbeta[rows])
+    st = parity.compare_quant(q[rows], s[rows], dec, label=f"weight sweep a={a}")
+    note(f"  {st}")
+
+
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_weight_prep_full_config(w, cfg):
     note(f"case: weight prep full config {cfg}")
@@ -339,6 +353,40 @@ def test_end_to_end_full_config(w, cfg):
     assert np.array_equal(yb, parity.bf16_rne(y32).astype(np.float64))
 
 
+@pytest.mark.parametrize("a", gen.SWEEP_A)
+def test_end_to_end_shared_factor_sweep(w, a):
+    """Config 5 (16384 x 4096 x 4096) end to end for every shared-factor size,
+    through the path the benchmark times (transform kernel, offline weight
+    prep and packing, the packed GEMM): sampled outputs against the oracle
+    chain (1e-3 relative, fp32 output), the fp32 bound elementwise on the
+    GPU's own operands, and bf16 = RNE(fp32)."""
+    note(f"case: end-to-end sweep a={a} (config 5)")
+    wl = gen.make_workload(5, a=a)
+    xq, xs = w.act_transform_quant(dev_bf16(wl.X_bits), dev_f32(wl.A), dev_f32(wl.B),
+                                   dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta)))
+    wq, ws = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    wp = w.weight_pack(wq, ws)
+    Y32 = w.mxfp4_gemm_packed(xq, xs, wp, out_dtype=torch.float32)
+    Yb = w.mxfp4_gemm_packed(xq, xs, wp, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = _sample_rows(wl.M, 40, 1500 + a)
+    cols = _sample_rows(wl.N, 40, 1600 + a)
+    x = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
+    wt = ob.weight_prep(wl.W_bits[cols], wl.A, wl.B, wl.walpha[cols], wl.wbeta[cols])
+    ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
+    y32 = Y32[rows][:, cols].cpu().numpy().astype(np.float64)
+    rel = np.abs(y32 - ref).max() / np.abs(ref).max()
+    note(f"  max rel err {rel:.3e}")
+    assert rel <= 1e-3
+    gx = ob.unpack_codes(xq[rows].cpu().numpy())
+    gw = ob.unpack_codes(wq[cols].cpu().numpy())
+    ref_g, abs_g = ob.gemm_rows_cols(gx, xs[rows].cpu().numpy(), gw, ws[cols].cpu().numpy(),
+                                     np.arange(len(rows)), np.arange(len(cols)))
+    assert np.all(np.abs(y32 - ref_g) <= parity.gemm_bound(abs_g, wl.K))
+    yb = Yb[rows][:, cols].float().cpu().numpy()
+    assert np.array_equal(yb, parity.bf16_rne(y32.astype(np.float32)))
+
+
 # ------------------------------------------------------- packed-weight GEMM
 
 
@@ -412,6 +460,35 @@ def test_packed_gemm_matches_oracle_and_unpacked(w, M, N, K):
     assert np.array_equal(yb, parity.bf16_rne(y32).astype(np.float64))
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 12288, 4096), (16384, 4096, 4096)])
+def test_timed_gemm_instance_matches_oracle(w, M, N, K):
+    """The kernel the benchmark times (two workgroups per CU, K / 256 = 16,
+    more than 256 tiles) at the up/gate and large-prefill shapes, on random
+    MXFP4 operands: sampled rows with every column against the oracle, the
+    fp32 bound elementwise, 1e-3 relative, and bf16 = RNE(fp32)."""
+    note(f"case: timed GEMM instance {M}x{N}x{K}")
+    assert w.packed_gemm_kernel(M, N, K) == 1
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    xc, xs = _rand_mx(rng, M, K)
+    wc, ws = _rand_mx(rng, N, K)
+    wp = w.weight_pack(torch.from_numpy(ob.pack_codes(wc)).to(DEV), torch.from_numpy(ws).to(DEV))
+    xq_d, xs_d = torch.from_numpy(ob.pack_codes(xc)).to(DEV), torch.from_numpy(xs).to(DEV)
+    y32 = w.mxfp4_gemm_packed(xq_d, xs_d, wp, out_dtype=torch.float32)
+    yb = w.mxfp4_gemm_packed(xq_d, xs_d, wp, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # rows of every 128-row tile position, the first and last tiles included
+    rows = np.unique(np.concatenate([_sample_rows(M, 40, M + K), np.arange(120, 136), [M - 129, M - 128]]))
+    ref, absum = ob.gemm_rows_cols(xc, xs, wc, ws, rows, np.arange(N))
+    got = y32[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    bound = parity.gemm_bound(absum, K)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert err.max() <= 1e-3 * np.abs(ref).max()
+    gotb = yb[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    assert np.array_equal(gotb, parity.bf16_rne(got.astype(np.float32)))
+    note(f"  rows {len(rows)}, max err / bound {float((err / np.maximum(bound, 1e-300)).max()):.3f}")
+
+
 def test_packed_gemm_unaligned_output(w):
     """Y rows not a whole number of 16-byte chunks: scalar store path."""
     note("case: packed gemm unaligned output")
@@ -440,6 +517,7 @@ def test_packed_end_to_end_full_config(w, cfg):
     wp = w.weight_pack(wq, ws)
     Yp = w.mxfp4_gemm_packed(xq, xs, wp, out_dtype=torch.bfloat16)
     Yu = w.mxfp4_gemm(xq, xs, wq, ws, out_dtype=torch.bfloat16)
+    Y32 = w.mxfp4_gemm_packed(xq, xs, wp, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(Yp, Yu)
     rows = _sample_rows(wl.M, 16, 700 + cfg)
@@ -447,10 +525,12 @@ def test_packed_end_to_end_full_config(w, cfg):
     x = ob.act_transform_quant(wl.X_bits[rows], wl.A, wl.B, wl.alpha, wl.beta)
     wt = ob.weight_prep(wl.W_bits[cols], wl.A, wl.B, wl.walpha[cols], wl.wbeta[cols])
     ref = ob.gemm(x.codes, x.scales, wt.codes, wt.scales)
-    y = Yp[rows][:, cols].float().cpu().numpy().astype(np.float64)
+    y = Y32[rows][:, cols].cpu().numpy().astype(np.float64)
     rel = np.abs(y - ref).max() / np.abs(ref).max()
     note(f"  max rel err {rel:.3e}")
-    assert rel <= 1e-2  # bf16 output rounding on top of the fp32 bound
+    assert rel <= 1e-3
+    yb = Yp[rows][:, cols].float().cpu().numpy()
+    assert np.array_equal(yb, parity.bf16_rne(y.astype(np.float32)))
 
 
 

@@ -460,17 +460,89 @@ def test_fp32_evaluation_only_flips_exempt_decisions():
         assert np.array_equal(codes[fixed], d.codes[fixed])
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def _window_case(y, S):
+    """Decisions of one 32-element block with hand-chosen exact values and
+    absolute sums (no clipping)."""
+    Y = np.zeros((1, 32))
+    A = np.zeros((1, 32))
+    Y[0, :len(y)] = y
+    A[0, :len(S)] = S
+    return ob.decisions(Y, A, None, None)
+
+
+def test_free_window_width_is_gamma36_of_the_abs_sum():
+    """An element is free exactly when its exact value lies within
+    beta = gamma_36 * S of a rounding boundary (S = sum |x||P|, the scale of
+    every fp32 error the transform can make), and the window grows with S,
+    not with |y|: checked on both sides of the boundary 0.75 at 0.9 beta and
+    1.1 beta, for two values of S.  A block's scale is free exactly when its
+    max lies within beta (plus the 2^-22 relative slack of the fp32 clip
+    bound) of a power of two."""
+    beta1 = ob.gamma(ob.ROUNDINGS) + 2.0 ** -45
+    assert ob.ROUNDINGS == 36 and abs(ob.gamma(36) / (36 * 2.0 ** -24) - 1) < 1e-5
+    for S in (1.0, 10.0):
+        beta = beta1 * S
+        for side in (+1, -1):
+            near = _window_case([6.0, 0.75 + side * 0.9 * beta], [6.0, S])
+            far = _window_case([6.0, 0.75 + side * 1.1 * beta], [6.0, S])
+            assert near.elem_free[0, 1] and not far.elem_free[0, 1], (S, side)
+            assert not near.block_free.any() and not far.block_free.any()
+    # same |y|, ten times the abs sum: 1.1 beta(S=1) is inside the wider window
+    assert _window_case([6.0, 0.75 + 1.1 * beta1], [6.0, 10.0]).elem_free[0, 1]
+    # the scale window around the power of two 4 (e flips from -1 to 0)
+    S = 4.0
+    beta = beta1 * S
+    for d, free in ((0.9, True), (1.2, False), (-0.9, True), (-1.1, False)):
+        dec = _window_case([4.0 + d * beta, 1.0], [S, 1.0])
+        assert bool(dec.block_free[0, 0]) == free, d
+
+
+def test_transform_abs_sum_is_the_sum_of_absolute_products():
+    """S = |x| |P| by hand on a block with cancellation (y = 0, S = 2) and the
+    bf16 oracle path carries it: an exact zero keeps both signs, nothing else
+    is free."""
+    P = np.eye(32)[None].copy()
+    P[0, 0, 0], P[0, 1, 0] = 1.0, 1.0  # y_0 = x_0 + x_1
+    X = np.zeros((1, 32))
+    X[0, 0], X[0, 1], X[0, 2] = 1.0, -1.0, 3.0
+    S = ob.transform_abs_sum(X, P)
+    assert S[0, 0] == 2.0 and S[0, 1] == 1.0 and S[0, 2] == 3.0
+    assert ob.transform(X, P)[0, 0] == 0.0
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_exempt_window_stays_narrow(cfg):
-    """The free set is the rigorous fp32 window (about 2e-6 of a block's absolute
-    sum); on these workloads it covers a few 1e-5 of the elements at most.  A
-    bound blown up by a slip (wrong gamma, S not in absolute values) fails here."""
-    M = {1: None, 2: 256, 3: 128, 4: None}[cfg]
+    """On the configs' inputs: the stated exempt set (elements within 1e-6
+    relative of a rounding boundary) is fewer than 1e-5 of the elements, as
+    the parity rule requires; the rigorous free set (gamma_36 S, a few 1e-6
+    of S; counted with every code of a free block) stays under 1.5e-5 plus
+    one block (a bound blown up by a slip, such as a wrong gamma or S not in
+    absolute values, fails here); no value is an exact zero."""
+    from tests import parity
+
+    M = {1: None, 2: 512, 3: 256, 4: None, 5: 512}[cfg]
     wl = gen.make_workload(cfg, M=M, with_weights=False)
     d = ob.act_transform_quant(wl.X_bits, wl.A, wl.B, wl.alpha, wl.beta)
     n = d.codes.size
-    assert d.n_exempt / n < 5e-5, (d.n_exempt, n)
+    n_lit = int(parity.literal_window(d).sum())
+    assert n_lit < 1e-5 * n or n_lit == 0, (n_lit, n)
+    assert d.n_exempt <= 1.5e-5 * n + 32, (d.n_exempt, n)
+    assert int(d.elem_free.sum()) <= 1.5e-5 * n + 1, (int(d.elem_free.sum()), n)
     assert not np.any(d.zero_sign_free)
+
+
+def test_literal_window_marks_values_near_boundaries():
+    """The stated window, by hand: 0.75 (1 + 5e-7) is inside, 0.75 (1 + 2e-6)
+    outside; 2.5 (1 - 9e-7) inside; a grid value (2) is far from any
+    boundary; with a block max of 12 (scale 2^1) the window applies to the
+    scaled value, so 2 (0.75) (1 + 5e-7) is inside."""
+    from tests import parity
+
+    dec = _window_case([6.0, 0.75 * (1 + 5e-7), 0.75 * (1 + 2e-6), 2.5 * (1 - 9e-7), 2.0], [6.0, 1, 1, 1, 1])
+    assert parity.literal_window(dec)[0, 1:5].tolist() == [True, False, True, False]
+    dec = _window_case([12.0, 1.5 * (1 + 5e-7), 1.5 * (1 + 3e-6)], [12.0, 1, 1])
+    assert dec.scales[0, 0] == 128
+    assert parity.literal_window(dec)[0, 1:3].tolist() == [True, False]
 
 
 def test_no_clip_is_the_plain_quantiser_and_tiny_blocks_use_the_lowest_scale():

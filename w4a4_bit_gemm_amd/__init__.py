@@ -27,4 +27,8 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     w4a4_decode,
     kv_cache_quant,
+    probe_mfma_fp4,
+    probe_stream_granule,
+    probe_hbm_read,
+    probe_hbm_copy,
 )

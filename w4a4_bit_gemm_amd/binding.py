@@ -73,6 +73,14 @@ def _load():
     lib.batq_kv_cache_quant.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, I32, P, P, P]
     lib.batq_decode_workspace_bytes.restype = I64
     lib.batq_decode_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.batq_probe_mfma_fp4.restype = ctypes.c_int
+    lib.batq_probe_mfma_fp4.argtypes = [I64, I32, I32, ctypes.c_uint32, P, P, P]
+    lib.batq_probe_stream_granule.restype = I64
+    lib.batq_probe_stream_granule.argtypes = []
+    lib.batq_probe_hbm_read.restype = ctypes.c_int
+    lib.batq_probe_hbm_read.argtypes = [P, I64, P, P]
+    lib.batq_probe_hbm_copy.restype = ctypes.c_int
+    lib.batq_probe_hbm_copy.argtypes = [P, P, I64, P]
     lib.batq_w4a4_decode.restype = ctypes.c_int
     lib.batq_w4a4_decode.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, P, ctypes.c_int, P, P, P, I64,
                                      P]
@@ -123,17 +131,79 @@ def _stream_ptr(torch, dev) -> int:
 
 
 def _req(t, dtype, name):
+    """Type, dtype and contiguity; the device is checked by :func:`_dev` once
+    every shape has been (so that the shape checks also run on the CPU)."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
+def _dev(*tensors):
+    """Every given tensor is on the same HIP device (the last check before a
+    call into the library)."""
+    devs = {t.device for t in tensors if t is not None}
+    for d in devs:
+        if d.type != "cuda":
+            raise ValueError("tensors must be CUDA (HIP) tensors")
+    if len(devs) > 1:
+        raise ValueError(f"tensors must be on one device, got {sorted(str(d) for d in devs)}")
+
+
 def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
+
+
+def _req_shape(t, dtype, shape, name):
+    """_req plus an exact shape; a wrong-sized buffer would otherwise turn
+    into out-of-bounds device reads or writes."""
+    _req(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+_FACTOR_SIZES = (1, 2, 4, 8, 16, 32)
+
+
+def _factors(A, B, K, names=("A", "B")):
+    """Checks the GPK factors against K: A [a, a] with a in {1,..,32}, B
+    [K/32, 32/a, 32/a], both float32 device tensors.  Returns (a, b)."""
+    torch = _torch()
+    _req(A, torch.float32, names[0])
+    _req(B, torch.float32, names[1])
+    if A.dim() != 2 or A.shape[0] != A.shape[1] or A.shape[0] not in _FACTOR_SIZES:
+        raise ValueError(f"{names[0]} must be [a, a] with a in {_FACTOR_SIZES}, got {tuple(A.shape)}")
+    a = int(A.shape[0])
+    b = 32 // a
+    if tuple(B.shape) != (K // 32, b, b):
+        raise ValueError(f"{names[1]} must be [K/32, {b}, {b}] = {(K // 32, b, b)}, got {tuple(B.shape)}")
+    return a, b
+
+
+def _ratios(r_hi, r_lo, shape, names=("r_hi", "r_lo")):
+    """Both None (no clipping) or both float32 device tensors of ``shape``."""
+    torch = _torch()
+    if (r_hi is None) != (r_lo is None):
+        raise ValueError(f"{names[0]} and {names[1]} must both be given or both be None")
+    if r_hi is not None:
+        _req_shape(r_hi, torch.float32, shape, names[0])
+        _req_shape(r_lo, torch.float32, shape, names[1])
+
+
+def _packed(Wp, name="Wp"):
+    torch = _torch()
+    if not isinstance(Wp, PackedWeight):
+        raise ValueError(f"{name} must be a PackedWeight (from weight_pack)")
+    _req_shape(Wp.data, torch.uint8, (weight_packed_bytes(Wp.N, Wp.K),), f"{name}.data")
+
+
+def _rows2d(X, dtype, name):
+    _req(X, dtype, name)
+    if X.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {tuple(X.shape)}")
 
 
 def act_transform_quant(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple] = None):
@@ -153,23 +223,19 @@ def act_transform_quant_mxfp8(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple
 
 def _act(X, A, B, r_hi, r_lo, out, fp8: bool):
     torch = _torch()
-    _req(X, torch.bfloat16, "X")
-    _req(A, torch.float32, "A")
-    _req(B, torch.float32, "B")
-    if (r_hi is None) != (r_lo is None):
-        raise ValueError("r_hi and r_lo must both be given or both be None")
-    if r_hi is not None:
-        _req(r_hi, torch.float32, "r_hi")
-        _req(r_lo, torch.float32, "r_lo")
+    _rows2d(X, torch.bfloat16, "X")
     M, K = X.shape
-    a, b = A.shape[0], B.shape[-1]
-    if B.shape[0] != K // 32 or (r_hi is not None and r_hi.numel() != K // 32):
-        raise ValueError("B / ratio shapes must match K/32 blocks")
+    a, b = _factors(A, B, K)
+    _ratios(r_hi, r_lo, (K // 32,))
+    qshape = (M, K if fp8 else K // 2)
     if out is None:
-        Xq = torch.empty((M, K if fp8 else K // 2), dtype=torch.uint8, device=X.device)
+        Xq = torch.empty(qshape, dtype=torch.uint8, device=X.device)
         Xs = torch.empty((M, K // 32), dtype=torch.uint8, device=X.device)
     else:
         Xq, Xs = out
+        _req_shape(Xq, torch.uint8, qshape, "Xq (out)")
+        _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (out)")
+    _dev(X, A, B, r_hi, r_lo, Xq, Xs)
     fn = _load().batq_act_transform_quant_mxfp8 if fp8 else _load().batq_act_transform_quant
     st = fn(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Xq), _ptr(Xs),
             _stream_ptr(torch, X.device))
@@ -184,25 +250,19 @@ def weight_prep(W, AinvT, BinvT, wr_hi=None, wr_lo=None, out: Optional[tuple] = 
     ratios or None.  Returns (Wq uint8 [N, K/2], Ws uint8 [N, K/32]).
     """
     torch = _torch()
-    _req(W, torch.bfloat16, "W")
-    _req(AinvT, torch.float32, "AinvT")
-    _req(BinvT, torch.float32, "BinvT")
-    if (wr_hi is None) != (wr_lo is None):
-        raise ValueError("wr_hi and wr_lo must both be given or both be None")
+    _rows2d(W, torch.bfloat16, "W")
     N, K = W.shape
-    if wr_hi is not None:
-        _req(wr_hi, torch.float32, "wr_hi")
-        _req(wr_lo, torch.float32, "wr_lo")
-        if tuple(wr_hi.shape) != (N, K // 32) or tuple(wr_lo.shape) != (N, K // 32):
-            raise ValueError("weight ratios must be [N, K/32]")
-    if BinvT.shape[0] != K // 32:
-        raise ValueError("BinvT must have K/32 blocks")
+    a, b = _factors(AinvT, BinvT, K, names=("AinvT", "BinvT"))
+    _ratios(wr_hi, wr_lo, (N, K // 32), names=("wr_hi", "wr_lo"))
     if out is None:
         Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
         Ws = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
     else:
         Wq, Ws = out
-    st = _load().batq_weight_prep(_ptr(W), N, K, W.stride(0), AinvT.shape[0], BinvT.shape[-1], _ptr(AinvT),
+        _req_shape(Wq, torch.uint8, (N, K // 2), "Wq (out)")
+        _req_shape(Ws, torch.uint8, (N, K // 32), "Ws (out)")
+    _dev(W, AinvT, BinvT, wr_hi, wr_lo, Wq, Ws)
+    st = _load().batq_weight_prep(_ptr(W), N, K, W.stride(0), a, b, _ptr(AinvT),
                                   _ptr(BinvT), _ptr(wr_hi), _ptr(wr_lo), _ptr(Wq), _ptr(Ws),
                                   _stream_ptr(torch, W.device))
     _check(st)
@@ -223,27 +283,33 @@ def prepare_weight(W, A_host, B_host, walpha_host=None, wbeta_host=None):
     return weight_prep(W, torch.from_numpy(AinvT).to(dev), torch.from_numpy(BinvT).to(dev), rh, rl)
 
 
-def mxfp4_gemm(Xq, Xs, Wq, Ws, out_dtype=None, out=None):
-    """Y = deq(Xq, Xs) deq(Wq, Ws)^T with FP32 accumulation; bf16 (default) or f32 out."""
+def _gemm_out(out, out_dtype, M, N, device):
+    """The output buffer [M, N] (bfloat16 or float32), allocated or checked."""
     torch = _torch()
-    for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
-        _req(t, torch.uint8, n)
-    M, K2 = Xq.shape
-    N = Wq.shape[0]
-    K = 2 * K2
-    if Wq.shape[1] != K2 or tuple(Xs.shape) != (M, K // 32) or tuple(Ws.shape) != (N, K // 32):
-        raise ValueError("operand shapes do not match")
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out_dtype must be bfloat16 or float32")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
+        out = torch.empty((M, N), dtype=out_dtype, device=device)
     else:
-        _req(out, out_dtype, "out")
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+        _req_shape(out, out_dtype, (M, N), "out")
+    return out, out_dtype
+
+
+def mxfp4_gemm(Xq, Xs, Wq, Ws, out_dtype=None, out=None):
+    """Y = deq(Xq, Xs) deq(Wq, Ws)^T with FP32 accumulation; bf16 (default) or f32 out."""
+    torch = _torch()
+    for t, n in ((Xq, "Xq"), (Xs, "Xs"), (Wq, "Wq"), (Ws, "Ws")):
+        _rows2d(t, torch.uint8, n)
+    M, K2 = Xq.shape
+    N = Wq.shape[0]
+    K = 2 * K2
+    if Wq.shape[1] != K2 or tuple(Xs.shape) != (M, K // 32) or tuple(Ws.shape) != (N, K // 32):
+        raise ValueError("operand shapes do not match")
+    out, out_dtype = _gemm_out(out, out_dtype, M, N, Xq.device)
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    _dev(Xq, Xs, Wq, Ws, out)
     st = _load().batq_mxfp4_gemm(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), M, N, K, _ptr(out), code,
                                  _stream_ptr(torch, Xq.device))
     _check(st)
@@ -268,15 +334,18 @@ def weight_pack(Wq, Ws, out=None) -> PackedWeight:
     """Offline: repack MXFP4 weights (from :func:`weight_prep`) for
     :func:`mxfp4_gemm_packed`.  Needs K % 256 == 0."""
     torch = _torch()
-    _req(Wq, torch.uint8, "Wq")
-    _req(Ws, torch.uint8, "Ws")
+    _rows2d(Wq, torch.uint8, "Wq")
     N, K2 = Wq.shape
     K = 2 * K2
+    _req_shape(Ws, torch.uint8, (N, K // 32), "Ws")
     nbytes = weight_packed_bytes(N, K)
     if nbytes < 0:
         raise ValueError("packed weights need K to be a positive multiple of 256")
     if out is None:
         out = torch.empty((nbytes,), dtype=torch.uint8, device=Wq.device)
+    else:
+        _req_shape(out, torch.uint8, (nbytes,), "out")
+    _dev(Wq, Ws, out)
     _check(_load().batq_weight_pack(_ptr(Wq), _ptr(Ws), N, K, _ptr(out), _stream_ptr(torch, Wq.device)))
     return PackedWeight(out, N, K)
 
@@ -285,20 +354,17 @@ def mxfp4_gemm_packed(Xq, Xs, Wp: PackedWeight, out_dtype=None, out=None):
     """Y = deq(Xq, Xs) deq(W)^T with W packed by :func:`weight_pack`; same
     result as :func:`mxfp4_gemm` on the unpacked weight."""
     torch = _torch()
-    _req(Xq, torch.uint8, "Xq")
-    _req(Xs, torch.uint8, "Xs")
+    _rows2d(Xq, torch.uint8, "Xq")
+    _packed(Wp)
     M, K2 = Xq.shape
     K = 2 * K2
-    if K != Wp.K or tuple(Xs.shape) != (M, K // 32):
+    if K != Wp.K:
         raise ValueError("operand shapes do not match")
+    _req_shape(Xs, torch.uint8, (M, K // 32), "Xs")
     N = Wp.N
-    if out_dtype is None:
-        out_dtype = torch.bfloat16 if out is None else out.dtype
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=Xq.device)
-    else:
-        _req(out, out_dtype, "out")
+    out, out_dtype = _gemm_out(out, out_dtype, M, N, Xq.device)
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    _dev(Xq, Xs, Wp.data, out)
     st = _load().batq_mxfp4_gemm_packed(_ptr(Xq), _ptr(Xs), _ptr(Wp.data), M, N, K, _ptr(out), code,
                                         _stream_ptr(torch, Xq.device))
     _check(st)
@@ -309,19 +375,16 @@ def mxfp8_gemm_packed(Xq8, Xs, Wp: PackedWeight, out_dtype=None, out=None):
     """W4A8: Y = deq8(Xq8, Xs) deq4(W)^T with W packed by :func:`weight_pack`
     and MXFP8 (E4M3) activation codes from :func:`act_transform_quant_mxfp8`."""
     torch = _torch()
-    _req(Xq8, torch.uint8, "Xq8")
-    _req(Xs, torch.uint8, "Xs")
+    _rows2d(Xq8, torch.uint8, "Xq8")
+    _packed(Wp)
     M, K = Xq8.shape
-    if K != Wp.K or tuple(Xs.shape) != (M, K // 32):
+    if K != Wp.K:
         raise ValueError("operand shapes do not match")
+    _req_shape(Xs, torch.uint8, (M, K // 32), "Xs")
     N = Wp.N
-    if out_dtype is None:
-        out_dtype = torch.bfloat16 if out is None else out.dtype
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=Xq8.device)
-    else:
-        _req(out, out_dtype, "out")
+    out, out_dtype = _gemm_out(out, out_dtype, M, N, Xq8.device)
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    _dev(Xq8, Xs, Wp.data, out)
     st = _load().batq_mxfp8_gemm_packed(_ptr(Xq8), _ptr(Xs), _ptr(Wp.data), M, N, K, _ptr(out), code,
                                         _stream_ptr(torch, Xq8.device))
     _check(st)
@@ -363,28 +426,23 @@ def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None
     receive the quantised activations.  Returns Y [M, N].
     """
     torch = _torch()
-    _req(X, torch.bfloat16, "X")
-    _req(A, torch.float32, "A")
-    _req(B, torch.float32, "B")
-    if (r_hi is None) != (r_lo is None):
-        raise ValueError("r_hi and r_lo must both be given or both be None")
-    if r_hi is not None:
-        _req(r_hi, torch.float32, "r_hi")
-        _req(r_lo, torch.float32, "r_lo")
-    _req(workspace, torch.uint8, "workspace")
+    _rows2d(X, torch.bfloat16, "X")
     M, K = X.shape
+    a, b = _factors(A, B, K)
+    _ratios(r_hi, r_lo, (K // 32,))
+    _packed(Wp)
+    _req(workspace, torch.uint8, "workspace")
     if K != Wp.K:
         raise ValueError("X and the packed weight disagree on K")
     N = Wp.N
-    if out_dtype is None:
-        out_dtype = torch.bfloat16 if out is None else out.dtype
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    else:
-        _req(out, out_dtype, "out")
+    out, out_dtype = _gemm_out(out, out_dtype, M, N, X.device)
     Xq, Xs = quantized_out if quantized_out is not None else (None, None)
+    if quantized_out is not None:
+        _req_shape(Xq, torch.uint8, (M, K // 2), "Xq (quantized_out)")
+        _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (quantized_out)")
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
-    st = _load().batq_w4a4_decode(_ptr(X), M, K, X.stride(0), A.shape[0], B.shape[-1], _ptr(A), _ptr(B),
+    _dev(X, A, B, r_hi, r_lo, Wp.data, workspace, out, Xq, Xs)
+    st = _load().batq_w4a4_decode(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B),
                                   _ptr(r_hi), _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
                                   _ptr(workspace), workspace.numel(), _stream_ptr(torch, X.device))
     _check(st)
@@ -397,20 +455,60 @@ def kv_cache_quant(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s, fmt: int = 4):
     MXFP4) or [rows, H*D] (fmt 8, MXFP8 E4M3) uint8, cache_s [rows, H*D/32]
     uint8.  Rows of the cache not named by a slot are left untouched."""
     torch = _torch()
-    _req(KV, torch.bfloat16, "KV")
-    _req(A, torch.float32, "A")
-    _req(B, torch.float32, "B")
-    _req(slots, torch.int64, "slots")
-    _req(cache_q, torch.uint8, "cache_q")
-    _req(cache_s, torch.uint8, "cache_s")
-    if (r_hi is None) != (r_lo is None):
-        raise ValueError("r_hi and r_lo must both be given or both be None")
+    _rows2d(KV, torch.bfloat16, "KV")
     T, HD = KV.shape
+    a, b = _factors(A, B, HD)
+    _ratios(r_hi, r_lo, (HD // 32,))
+    _req_shape(slots, torch.int64, (T,), "slots")
+    _rows2d(cache_q, torch.uint8, "cache_q")
     rows = cache_q.shape[0]
-    if fmt not in (4, 8) or tuple(cache_q.shape) != (rows, HD if fmt == 8 else HD // 2) \
-            or tuple(cache_s.shape) != (rows, HD // 32) or slots.numel() != T:
-        raise ValueError("cache / slot shapes do not match")
-    st = _load().batq_kv_cache_quant(_ptr(KV), T, HD, KV.stride(0), A.shape[0], B.shape[-1], _ptr(A), _ptr(B),
+    if fmt not in (4, 8):
+        raise ValueError("fmt must be 4 (MXFP4) or 8 (MXFP8)")
+    _req_shape(cache_q, torch.uint8, (rows, HD if fmt == 8 else HD // 2), "cache_q")
+    _req_shape(cache_s, torch.uint8, (rows, HD // 32), "cache_s")
+    _dev(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s)
+    st = _load().batq_kv_cache_quant(_ptr(KV), T, HD, KV.stride(0), a, b, _ptr(A), _ptr(B),
                                      _ptr(r_hi), _ptr(r_lo), _ptr(slots), rows, fmt, _ptr(cache_q), _ptr(cache_s),
                                      _stream_ptr(torch, KV.device))
     _check(st)
+
+
+# ------------------------------------------------ measurement probes (batq_probe.h)
+
+
+def probe_mfma_fp4(workgroups: int, iters: int, random_data: int, seed: int, sink, clocks):
+    """FP4 MFMA register loop: sink float32 [4 * workgroups], clocks int64
+    [8 * workgroups] (shader cycles and 100 MHz ticks per wave)."""
+    torch = _torch()
+    _req_shape(sink, torch.float32, (4 * workgroups,), "sink")
+    _req_shape(clocks, torch.int64, (8 * workgroups,), "clocks")
+    _dev(sink, clocks)
+    _check(_load().batq_probe_mfma_fp4(workgroups, iters, random_data, seed, _ptr(sink), _ptr(clocks),
+                                       _stream_ptr(torch, sink.device)))
+
+
+def probe_stream_granule() -> int:
+    """Stream sizes of the HBM probes are multiples of this many bytes."""
+    return int(_load().batq_probe_stream_granule())
+
+
+def probe_hbm_read(src, sink):
+    """Streaming read of all of src (any dtype, contiguous); sink int32 [2048]."""
+    torch = _torch()
+    _req(src, src.dtype, "src")
+    _req_shape(sink, torch.int32, (2048,), "sink")
+    _dev(src, sink)
+    _check(_load().batq_probe_hbm_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                       _stream_ptr(torch, src.device)))
+
+
+def probe_hbm_copy(src, dst):
+    """Streaming copy of src into dst (same number of bytes, contiguous)."""
+    torch = _torch()
+    _req(src, src.dtype, "src")
+    _req(dst, dst.dtype, "dst")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must have the same size in bytes")
+    _dev(src, dst)
+    _check(_load().batq_probe_hbm_copy(_ptr(src), _ptr(dst), nb, _stream_ptr(torch, src.device)))

@@ -1,4 +1,10 @@
-"""Build libbatq.so (all HIP sources, gfx950) in-tree with hipcc."""
+"""Build libbatq.so (all HIP sources, gfx950) in-tree with hipcc.
+
+Each source compiles to its own object in parallel (the GEMM files fully
+unroll their stage loops and dominate the time), then one link makes the
+shared library.  Objects go to a scratch folder beside the package and are
+rebuilt on every call.
+"""
 from __future__ import annotations
 
 import glob
@@ -6,17 +12,18 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libbatq.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 
-HIPCC_FLAGS = [
+COMPILE_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     # packed FP32 math stays off (the compiler would otherwise emit v_pk_* ops)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -24,6 +31,7 @@ HIPCC_FLAGS = [
     # the GEMM kernels fully unroll their stage loops for common K (exact wait counts)
     "-mllvm", "-pragma-unroll-threshold=1000000",
 ]
+LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC"]
 
 
 def hipcc() -> str:
@@ -33,22 +41,40 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           *srcs, "-o", tmp]
+def _filter(stderr: str) -> str:
+    return "\n".join(ln for ln in stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip())
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMPILE_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+           "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip())
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err:
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({res.returncode}):\n{_filter(res.stderr)}")
+    if verbose and _filter(res.stderr):
+        print(_filter(res.stderr), file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *LINK_FLAGS, *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_filter(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="-v" in sys.argv))

@@ -420,12 +420,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // Codes: instruction q of this wave fills LDS bytes [1024 (8 wave + q),
   // +1024) = rows 4 (8 wave + q) + l / 16; lane l fetches the row's chunk
   // (l % 16) ^ (row % 16) for position l % 16.  The swizzle repeats every
-  // four instructions, so four lane offsets serve all eight, the rest of the
-  // row offset going into the scalar offset.  Rows past M lie past the end of
-  // the descriptor's range and read zeros; they are never stored.
+  // four instructions, so four lane offsets serve all eight: instructions
+  // 4..7 (rows 16 further on) use a second descriptor based 16 rows later.
+  // The whole row offset is in the vector offset, which the range check
+  // covers, so rows past M read zeros without touching memory; they are
+  // never stored.
   const uint32_t krow = (uint32_t)p.K;
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, (short)0, (int)(p.M * (int64_t)krow), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs16 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.xq + 16 * (int64_t)krow), (short)0, p.M > 16 ? (int)((p.M - 16) * (int64_t)krow) : 0, 0x00020000);
   uint32_t qoff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -441,13 +445,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const int64_t gr = m0 + row < p.M ? m0 + row : p.M - 1;
     soff = (uint32_t)gr * srow + 16u * (uint32_t)(lane >> 5);
   }
-  const uint32_t k16 = 16 * krow;  // 16 rows
 #define DMA_A8(SLOT, ST)                                                                        \
   {                                                                                            \
     const uint32_t st_ = (uint32_t)opaque_stage((ST) * kRowBytes8);                            \
     _Pragma("unroll") for (int q = 0; q < kQPerWave8; ++q)                                      \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)((SLOT) + 1024 * (kQPerWave8 * wave + q)), 16, \
-                                               (int)qoff[q & 3], (int)((q >> 2) * k16 + st_), 0, 0);        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((q >> 2) ? xrs16 : xrs,                         \
+                                               (lds_void*)((SLOT) + 1024 * (kQPerWave8 * wave + q)), 16, \
+                                               (int)qoff[q & 3], (int)st_, 0, 0);               \
   }
 #define DMA_S8(SG, G) \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)((SG) + 1024 * wave), 16, (int)soff, (int)((G) * 32), 0, 0);

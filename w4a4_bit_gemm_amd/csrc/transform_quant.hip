@@ -26,7 +26,8 @@
 // sign-preserving) on z * 2^-e, which is exact.
 //
 // The same kernel also produces MXFP8 (E4M3) codes for the W4A8 setting
-// [nubint.ai review, Table 2]: e = floor(log2 max|z|) - 8 (the largest E4M3
+// [nubint.ai review, Table 2; en.papernotes.org, Loss & Training: E4M3
+// elements]: e = floor(log2 max|z|) - 8 (the largest E4M3
 // exponent), one byte per element.  Its converter v_cvt_scalef32_pk_fp8_f32
 // rounds to nearest even with subnormals but does not saturate (it returns the
 // NaN code above 448), so z is clamped to +-448 * 2^e first, which leaves the
@@ -145,13 +146,15 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
 
   const bool loader = wave == kLoaderWave;
   // Loader: tile i (< ntile) -> its slot, kTT / 2 load instructions per tile.
-  // Addressing: a buffer descriptor based at the tile's first row whose
-  // size ends at the last row of X (the hardware range check turns rows past
-  // the end into zeros, which are never stored), plus per-lane byte offsets
-  // within the tile.  Instruction q covers rows 2q and 2q + 1: lane l fetches
-  // row 2q + l / 32, logical 16-byte chunk c = (l % 32) ^ (row % 16) (chunks
-  // past K read a valid column, unused).  The swizzle repeats every 8
-  // instructions, so 8 offsets serve all 16; rows 16..31 add a scalar offset.
+  // Addressing: per-lane byte offsets within a 16-row half tile, against a
+  // buffer descriptor based at that half's first row whose size ends at the
+  // last byte of X.  The whole row offset is in the vector offset, which the
+  // hardware range check covers, so rows past the end read zeros (never
+  // stored) without touching memory.  Instruction q covers rows 2q and
+  // 2q + 1: lane l fetches row 2q + l / 32, logical 16-byte chunk
+  // c = (l % 32) ^ (row % 16) (chunks past K read a valid column, unused).
+  // The swizzle repeats every 8 instructions, so the same 8 offsets serve
+  // both halves, rows 16..31 through the second descriptor.
   const uint32_t ld2 = (uint32_t)(p.ldx * 2);  // row stride in bytes
   uint32_t voff[8];
 #pragma unroll
@@ -164,15 +167,20 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
   const uint8_t* const xb = reinterpret_cast<const uint8_t*>(p.x);
   auto load_tile = [&](int64_t i, int slot) {
     const int64_t tok0 = (ty0 + i * tstep) * kTT;
-    const int64_t left = (p.rows - tok0) * (int64_t)ld2;  // bytes from the tile's first row to the end of X
-    const int nrec = left < 0x7FFFFFFF ? (int)left : 0x7FFFFFFF;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(xb + tok0 * (int64_t)ld2), (short)0, nrec, 0x00020000);
     uint8_t* dst = xs + slot * T::kX;
 #pragma unroll
-    for (int q = 0; q < kTT / 2; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + q * 1024), 16, (int)voff[q & 7],
-                                               (int)((q >> 3) * 16 * ld2), 0, kXPolicy);
+    for (int half = 0; half < 2; ++half) {
+      const int64_t row0 = tok0 + 16 * half;
+      // bytes from the half tile's first row to the end of X (none: every load reads zeros)
+      const int64_t left = row0 < p.rows ? (p.rows - row0) * (int64_t)ld2 : 0;
+      const int nrec = left < 0x7FFFFFFF ? (int)left : 0x7FFFFFFF;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(xb + row0 * (int64_t)ld2), (short)0, nrec, 0x00020000);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (8 * half + q) * 1024), 16, (int)voff[q],
+                                                 0, 0, kXPolicy);
+    }
   };
   // The first tiles are requested before anything else, so that their latency
   // overlaps the factor and ratio loads below (loads issued after them only
