@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BATQ_ABI_VERSION 1
+#define BATQ_ABI_VERSION 2
 
 typedef enum {
   BATQ_OK = 0,
@@ -55,7 +55,9 @@ typedef enum {
                                alignment                                          */
   BATQ_ERR_UNSUPPORTED = 4, /* a outside {1,2,4,8,16,32} or unknown output type   */
   BATQ_ERR_SINGULAR = 5,    /* a factor is singular or too ill-conditioned        */
-  BATQ_ERR_HIP = 6          /* the HIP runtime rejected a launch                  */
+  BATQ_ERR_HIP = 6,         /* the HIP runtime rejected a launch                  */
+  BATQ_ERR_TOO_LARGE = 7    /* the problem needs more scratch than the
+                               no-allocation entry point holds                    */
 } batq_status;
 
 typedef enum { BATQ_OUT_BF16 = 0, BATQ_OUT_F32 = 1 } batq_out_dtype;
@@ -268,6 +270,35 @@ batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t l
                              const float* A, const float* B, const float* r_hi, const float* r_lo,
                              const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq, uint8_t* Xs,
                              void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ fused decode, no allocation
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same computation, kernels and results (bit for bit) as
+ * batq_w4a4_decode; the fp32 partial tiles go to a device array inside the
+ * library instead of a caller workspace.
+ */
+
+/* Size of that array: BATQ_ERR_TOO_LARGE for any (M, N, K) whose
+ * batq_decode_workspace_bytes exceeds it.  Host only. */
+int64_t batq_decode_noalloc_scratch_bytes(void);
+
+/* As batq_w4a4_decode, without the workspace arguments.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  The first
+ * call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, with the device current; the device of the calling
+ * thread must be the stream's device, as for any launch) and keeps its
+ * address; each GPU holds its copy until the process ends.  Every call on a
+ * GPU shares that GPU's array and overwrites what it reads, so nothing needs
+ * clearing between calls, but calls that overlap on one GPU (other streams,
+ * other threads) race: serialise them.  The array keeps the last call's
+ * partials.
+ * Errors: as batq_w4a4_decode; TOO_LARGE (see above); HIP (also the address
+ * lookup failing). */
+batq_status batq_w4a4_decode_noalloc(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
+                                     const float* A, const float* B, const float* r_hi, const float* r_lo,
+                                     const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq,
+                                     uint8_t* Xs, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ from tests.conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "batq.h")
 
-OK, NULL, SHAPE, ALIGN, UNSUP, SINGULAR, HIP = range(7)
+OK, NULL, SHAPE, ALIGN, UNSUP, SINGULAR, HIP, TOO_LARGE = range(8)
 FAKE = 0x10000  # aligned address never dereferenced: every case below fails a check first
 
 
@@ -52,8 +52,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.batq_abi_version() == 1
-    for s in range(7):
+    assert lib.batq_abi_version() == 2
+    for s in range(8):
         assert lib.batq_status_str(s) and lib.batq_status_str(s) != b"unknown status"
     assert lib.batq_status_str(99) == b"unknown status"
 

@@ -73,6 +73,11 @@ def _load():
     lib.batq_kv_cache_quant.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, I32, P, P, P]
     lib.batq_decode_workspace_bytes.restype = I64
     lib.batq_decode_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.batq_decode_noalloc_scratch_bytes.restype = I64
+    lib.batq_decode_noalloc_scratch_bytes.argtypes = []
+    lib.batq_w4a4_decode_noalloc.restype = ctypes.c_int
+    lib.batq_w4a4_decode_noalloc.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, P, ctypes.c_int, P, P,
+                                             P]
     lib.batq_probe_mfma_fp4.restype = ctypes.c_int
     lib.batq_probe_mfma_fp4.argtypes = [I64, I32, I32, ctypes.c_uint32, P, P, P]
     lib.batq_probe_stream_granule.restype = I64
@@ -449,6 +454,41 @@ def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None
     return out
 
 
+def decode_noalloc_scratch_bytes() -> int:
+    """Size of the library's scratch array for :func:`w4a4_decode_noalloc`."""
+    return int(_load().batq_decode_noalloc_scratch_bytes())
+
+
+def w4a4_decode_noalloc(X, A, B, r_hi, r_lo, Wp: PackedWeight, out, quantized_out: Optional[tuple] = None):
+    """:func:`w4a4_decode` for callers that cannot allocate: the same result,
+    with the partial tiles in the library's own device array instead of a
+    workspace.  ``out`` ([M, N] bf16 or float32) is required, so that nothing
+    is allocated on this path either.  Calls that overlap on one GPU race."""
+    torch = _torch()
+    _rows2d(X, torch.bfloat16, "X")
+    M, K = X.shape
+    a, b = _factors(A, B, K)
+    _ratios(r_hi, r_lo, (K // 32,))
+    _packed(Wp)
+    if K != Wp.K:
+        raise ValueError("X and the packed weight disagree on K")
+    N = Wp.N
+    if out is None:
+        raise ValueError("out is required (this path allocates nothing)")
+    out, out_dtype = _gemm_out(out, None, M, N, X.device)
+    Xq, Xs = quantized_out if quantized_out is not None else (None, None)
+    if quantized_out is not None:
+        _req_shape(Xq, torch.uint8, (M, K // 2), "Xq (quantized_out)")
+        _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (quantized_out)")
+    _dev(X, A, B, r_hi, r_lo, Wp.data, out, Xq, Xs)
+    code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
+    st = _load().batq_w4a4_decode_noalloc(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi),
+                                          _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
+                                          _stream_ptr(torch, X.device))
+    _check(st)
+    return out
+
+
 def kv_cache_quant(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s, fmt: int = 4):
     """Quantise new K or V rows into a cache: KV [T, H*D] bf16 (head_dim a
     multiple of 32), slots [T] int64 cache rows, cache_q [rows, H*D/2] (fmt 4,
@@ -512,3 +552,4 @@ def probe_hbm_copy(src, dst):
         raise ValueError("src and dst must have the same size in bytes")
     _dev(src, dst)
     _check(_load().batq_probe_hbm_copy(_ptr(src), _ptr(dst), nb, _stream_ptr(torch, src.device)))
+

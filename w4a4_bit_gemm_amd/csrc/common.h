@@ -100,4 +100,9 @@ struct DecodeArgs {
 };
 int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_decode_fused(const DecodeArgs& args, hipStream_t stream);
+// The no-allocation decode path's partial tiles: a device array of this many
+// bytes (decode_fused.hip), whose address on the current device
+// decode_scratch returns (looked up once per device).
+constexpr int64_t kDecodeScratchBytes = 16ll << 20;
+hipError_t decode_scratch(void** ptr);
 }  // namespace batq

@@ -23,11 +23,23 @@
 // decode_reduce_kernel then sums the splits of every output in split order
 // (deterministic) and writes Y.  The launch boundary orders the two, so no
 // workgroup ever waits for or synchronises with another.
+#include <mutex>
+
 #include "block_quant.h"
 
 namespace batq {
 
 namespace {
+
+// Scratch of the no-allocation entry point (batq_w4a4_decode_noalloc): the
+// fp32 partial tiles go to this device array instead of a caller workspace.
+// Each GPU holds its own copy until the process ends.  On the host the name is
+// only a stand-in, never an address: host code uses the pointer that
+// hipGetSymbolAddress returns for the current device (decode_scratch below).
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
 
 constexpr int kQRow = 144;  // staged code row: 8 blocks x 16 bytes + 16 pad (conflict-free reads)
 
@@ -243,6 +255,22 @@ int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t nchunk = (N + 255) / 256, nst = K / 256;
   const int spw = stages_per_wg(M, nchunk, nst);
   return nchunk * ((nst + spw - 1) / spw) * M * 256 * 4;
+}
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_fused(const DecodeArgs& args, hipStream_t stream) {
