@@ -393,11 +393,13 @@ def calibrate_copy(torch, dev, steps):
                       "launches": 2 * steps, "GB/s": 8 * n / dt / 1e9}), flush=True)
 
 
-def measure_ceilings(torch, w, dev):
+def measure_ceilings(torch, w, dev, act_read_bytes=None, act_write_ratio=4):
     """The ceilings the kernels are set against, measured on this GPU: the
     block-scaled FP4 MFMA in a register-only loop (random and constant operand
-    bits, 2 and 1 waves per SIMD) with the shader clock it ran at, and HBM
-    read and copy streams over buffers eight times the Infinity Cache."""
+    bits, 2 and 1 waves per SIMD) with the shader clock it ran at, HBM read
+    and copy streams over buffers eight times the Infinity Cache, and a
+    stream shaped like the activation transform's traffic (its bf16 bytes
+    read, a quarter as many written) over buffers rotated past the cache."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     mf = {}
     iters = 20000
@@ -442,7 +444,24 @@ def measure_ceilings(torch, w, dev):
     read = stream(lambda: w.probe_hbm_read(src, rsink), nbytes)
     copy = stream(lambda: w.probe_hbm_copy(csrc, cdst), 2 * (nbytes // 2))
     del src, cdst
-    return {"mfma_fp4_loop": mf, "hbm_read_GBs": read, "hbm_copy_GBs": copy,
+    shaped = None
+    if act_read_bytes:
+        rb = -(-act_read_bytes // gran) * gran
+        nbuf = max(2, -(-int(2.2 * CACHE_BYTES) // (rb + rb // act_write_ratio)))
+        bufs = [(torch.empty(rb // 4, dtype=torch.int32, device=dev),
+                 torch.empty(rb // act_write_ratio // 4, dtype=torch.int32, device=dev)) for _ in range(nbuf)]
+        k = [0]
+
+        def one():
+            s_, d_ = bufs[k[0] % nbuf]
+            k[0] += 1
+            w.probe_hbm_stream(s_, d_, act_write_ratio)
+
+        gbs = stream(one, rb + rb // act_write_ratio, reps=4 * nbuf)
+        shaped = {"read_bytes": rb, "write_bytes": rb // act_write_ratio, "GBs": gbs,
+                  "us": (rb + rb // act_write_ratio) / gbs / 1e3}
+        del bufs
+    return {"mfma_fp4_loop": mf, "hbm_read_GBs": read, "hbm_copy_GBs": copy, "act_shaped_stream": shaped,
             "note": "FP4 32x32x64 block-scaled MFMA, 8 independent chains per wave, no memory traffic; clock = "
                     "s_memtime cycles per s_memrealtime tick x 100 MHz; HBM read of 2 GiB, copy of 1 GiB -> 1 GiB"}
 
@@ -644,10 +663,11 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_ceiling:
-        ceil = measure_ceilings(torch, w, dev)
+        ceil = measure_ceilings(torch, w, dev, act_read_bytes=M * K * 2, act_write_ratio=2 if fp8 else 4)
         out["ceilings"] = ceil
         out["kernels"]["gemm"]["frac_of_mfma_loop"] = gemm_tflops / ceil["mfma_fp4_loop"]["random_2w_TFLOPs"]
         out["kernels"]["transform_quant"]["frac_of_hbm_read"] = act_gbs / ceil["hbm_read_GBs"]
+        out["kernels"]["transform_quant"]["frac_of_shaped_stream"] = ceil["act_shaped_stream"]["us"] / (t_act * 1e6)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds, "e4m3" if fp8 else "e2m1")
     print(json.dumps(out), flush=True)

@@ -33,13 +33,14 @@ extern "C" {
 batq_status batq_probe_mfma_fp4(int64_t workgroups, int32_t iters, int32_t random_data, uint32_t seed, float* sink,
                                 unsigned long long* clocks, hipStream_t stream);
 
-/* Stream sizes must be positive multiples of this many bytes (2048 workgroups
- * x 256 threads x 8 loads x 16 bytes). */
+/* Stream sizes must be positive multiples of this many bytes (256 threads x 8
+ * loads x 16 bytes); a stream runs on up to 2048 workgroups, each reading a
+ * contiguous range. */
 int64_t batq_probe_stream_granule(void);
 
-/* Reads `bytes` of src (16-byte aligned) once with 16-byte loads, 2048
- * workgroups each streaming a contiguous range; sink receives one xor word per
- * workgroup (2048 uint32).  Errors: SHAPE (bytes not a multiple of the
+/* Reads `bytes` of src (16-byte aligned) once with 16-byte loads, each
+ * workgroup streaming a contiguous range; sink receives one xor word per
+ * workgroup (room for 2048 uint32).  Errors: SHAPE (bytes not a multiple of the
  * granule), NULL, ALIGN, HIP. */
 batq_status batq_probe_hbm_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
@@ -47,6 +48,15 @@ batq_status batq_probe_hbm_read(const void* src, int64_t bytes, uint32_t* sink, 
  * 16-byte loads and stores, same split as batq_probe_hbm_read.
  * Errors: SHAPE, NULL, ALIGN, HIP. */
 batq_status batq_probe_hbm_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+/* A read:write stream: reads `read_bytes` of src once and writes
+ * read_bytes / ratio bytes to dst (each written 16-byte word the xor of
+ * `ratio` read words), same split as batq_probe_hbm_read.  ratio 4 is the mix
+ * of the activation transform (bf16 in, MXFP4 codes out).
+ * Errors: SHAPE (read_bytes not a multiple of the granule), UNSUPPORTED (ratio
+ * not 1, 2, 4 or 8), NULL, ALIGN, HIP. */
+batq_status batq_probe_hbm_stream(const void* src, int64_t read_bytes, void* dst, int32_t ratio,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

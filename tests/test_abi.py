@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
               "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
               "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode",
               "batq_kv_cache_quant", "batq_packed_gemm_kernel", "batq_probe_mfma_fp4", "batq_probe_hbm_read",
-              "batq_probe_hbm_copy", "batq_probe_stream_granule"):
+              "batq_probe_hbm_copy", "batq_probe_stream_granule", "batq_probe_hbm_stream"):
         assert n in names
 
 
@@ -262,14 +262,18 @@ def test_gpk_invert_rejects_singular(lib):
 
 def test_probe_argument_checks(lib):
     g = lib.batq_probe_stream_granule()
-    assert g == 2048 * 256 * 8 * 16
+    assert g == 256 * 8 * 16
     assert lib.batq_probe_mfma_fp4(0, 10, 1, 7, FAKE, FAKE, None) == SHAPE
     assert lib.batq_probe_mfma_fp4(4, 0, 1, 7, FAKE, FAKE, None) == SHAPE
     assert lib.batq_probe_mfma_fp4(4, 10, 1, 7, 0, FAKE, None) == NULL
     assert lib.batq_probe_mfma_fp4(4, 10, 1, 7, FAKE, FAKE + 4, None) == ALIGN
     assert lib.batq_probe_hbm_read(FAKE, g + 16, FAKE, None) == SHAPE
+    assert lib.batq_probe_hbm_read(FAKE, 0, FAKE, None) == SHAPE
     assert lib.batq_probe_hbm_read(0, g, FAKE, None) == NULL
     assert lib.batq_probe_hbm_read(FAKE + 8, g, FAKE, None) == ALIGN
     assert lib.batq_probe_hbm_copy(FAKE, FAKE, 0, None) == SHAPE
     assert lib.batq_probe_hbm_copy(FAKE, 0, g, None) == NULL
     assert lib.batq_probe_hbm_copy(FAKE, FAKE + 4, g, None) == ALIGN
+    assert lib.batq_probe_hbm_stream(FAKE, g, FAKE, 3, None) == UNSUP
+    assert lib.batq_probe_hbm_stream(FAKE, g - 16, FAKE, 4, None) == SHAPE
+    assert lib.batq_probe_hbm_stream(FAKE, g, 0, 4, None) == NULL

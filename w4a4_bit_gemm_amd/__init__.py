@@ -33,4 +33,5 @@ from .binding import (  # noqa: F401
     probe_stream_granule,
     probe_hbm_read,
     probe_hbm_copy,
+    probe_hbm_stream,
 )

@@ -84,6 +84,8 @@ def _load():
     lib.batq_probe_stream_granule.argtypes = []
     lib.batq_probe_hbm_read.restype = ctypes.c_int
     lib.batq_probe_hbm_read.argtypes = [P, I64, P, P]
+    lib.batq_probe_hbm_stream.restype = ctypes.c_int
+    lib.batq_probe_hbm_stream.argtypes = [P, I64, P, I32, P]
     lib.batq_probe_hbm_copy.restype = ctypes.c_int
     lib.batq_probe_hbm_copy.argtypes = [P, P, I64, P]
     lib.batq_w4a4_decode.restype = ctypes.c_int
@@ -553,3 +555,14 @@ def probe_hbm_copy(src, dst):
     _dev(src, dst)
     _check(_load().batq_probe_hbm_copy(_ptr(src), _ptr(dst), nb, _stream_ptr(torch, src.device)))
 
+
+def probe_hbm_stream(src, dst, ratio: int):
+    """Streaming read of all of src, writing a ratio-th of its bytes to dst."""
+    torch = _torch()
+    _req(src, src.dtype, "src")
+    _req(dst, dst.dtype, "dst")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nb // ratio:
+        raise ValueError("dst must hold read_bytes / ratio bytes")
+    _dev(src, dst)
+    _check(_load().batq_probe_hbm_stream(_ptr(src), nb, _ptr(dst), ratio, _stream_ptr(torch, src.device)))

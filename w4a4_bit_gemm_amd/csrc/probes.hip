@@ -122,14 +122,44 @@ __global__ __launch_bounds__(kStreamThreads) void probe_copy_kernel(const uint4*
   }
 }
 
-// Workgroups and 16-byte words per workgroup for a stream of `bytes`: a
-// multiple of 8 workgroups per CU, each range a whole number of rounds.
+// Reads `per` 16-byte words per workgroup and writes per / R, each written
+// word the xor of R read words (a read:write mix like the transform's, whose
+// bf16 rows are about four times its codes).
+template <int R>
+__global__ __launch_bounds__(kStreamThreads) void probe_stream_kernel(const uint4* __restrict__ src,
+                                                                      uint4* __restrict__ dst, int64_t per) {
+  static_assert(kUnroll % R == 0, "whole written words per round");
+  const int64_t rbase = (int64_t)blockIdx.x * per + threadIdx.x;
+  const int64_t wbase = (int64_t)blockIdx.x * (per / R) + threadIdx.x;
+  for (int64_t i = 0; i < per; i += kStreamThreads * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = src[rbase + i + u * kStreamThreads];
+#pragma unroll
+    for (int o = 0; o < kUnroll / R; ++o) {
+      uint4 x = v[o * R];
+#pragma unroll
+      for (int r = 1; r < R; ++r) {
+        x.x ^= v[o * R + r].x;
+        x.y ^= v[o * R + r].y;
+        x.z ^= v[o * R + r].z;
+        x.w ^= v[o * R + r].w;
+      }
+      dst[wbase + i / R + o * kStreamThreads] = x;
+    }
+  }
+}
+
+// Workgroups and 16-byte words per workgroup for a stream of `bytes`: up to
+// 2048 workgroups (8 per CU), each range a whole number of rounds of
+// kStreamThreads x kUnroll words.
 bool stream_split(int64_t bytes, int64_t& groups, int64_t& per) {
-  const int64_t words = bytes / 16;
   const int64_t round = (int64_t)kStreamThreads * kUnroll;
+  if (bytes <= 0 || bytes % (16 * round) != 0) return false;
+  const int64_t units = bytes / (16 * round);
   groups = 2048;
-  if (bytes <= 0 || bytes % 16 != 0 || words % (groups * round) != 0) return false;
-  per = words / groups;
+  while (groups > 1 && units % groups != 0) groups /= 2;
+  per = bytes / 16 / groups;
   return true;
 }
 
@@ -138,7 +168,7 @@ bool stream_split(int64_t bytes, int64_t& groups, int64_t& per) {
 
 extern "C" {
 
-int64_t batq_probe_stream_granule(void) { return 2048LL * 256 * 8 * 16; }
+int64_t batq_probe_stream_granule(void) { return 256LL * 8 * 16; }
 
 batq_status batq_probe_mfma_fp4(int64_t workgroups, int32_t iters, int32_t random_data, uint32_t seed, float* sink,
                                 unsigned long long* clocks, hipStream_t stream) {
@@ -168,6 +198,25 @@ batq_status batq_probe_hbm_copy(const void* src, void* dst, int64_t bytes, hipSt
   if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0) return BATQ_ERR_ALIGN;
   hipLaunchKernelGGL(batq::probe_copy_kernel, dim3((unsigned)groups), dim3(batq::kStreamThreads), 0, stream,
                      static_cast<const uint4*>(src), static_cast<uint4*>(dst), per);
+  return hipGetLastError() == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
+}
+
+batq_status batq_probe_hbm_stream(const void* src, int64_t read_bytes, void* dst, int32_t ratio,
+                                  hipStream_t stream) {
+  int64_t groups, per;
+  if (!batq::stream_split(read_bytes, groups, per)) return BATQ_ERR_SHAPE;
+  if (ratio != 1 && ratio != 2 && ratio != 4 && ratio != 8) return BATQ_ERR_UNSUPPORTED;
+  if (src == nullptr || dst == nullptr) return BATQ_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0) return BATQ_ERR_ALIGN;
+  const auto* s = static_cast<const uint4*>(src);
+  auto* d = static_cast<uint4*>(dst);
+  const dim3 g((unsigned)groups), b(batq::kStreamThreads);
+  switch (ratio) {
+    case 1: hipLaunchKernelGGL(batq::probe_stream_kernel<1>, g, b, 0, stream, s, d, per); break;
+    case 2: hipLaunchKernelGGL(batq::probe_stream_kernel<2>, g, b, 0, stream, s, d, per); break;
+    case 4: hipLaunchKernelGGL(batq::probe_stream_kernel<4>, g, b, 0, stream, s, d, per); break;
+    default: hipLaunchKernelGGL(batq::probe_stream_kernel<8>, g, b, 0, stream, s, d, per); break;
+  }
   return hipGetLastError() == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 
