@@ -215,6 +215,7 @@ def run_decode(args, torch, w, wl, dev):
     rl = None if args.no_clip else f32(w.clip_ratios(wl.beta))
     Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)  # offline
     Wp0 = w.weight_pack(Wq0, Ws0)
+    fac = w.decode_prepare_factors(A, B, K)  # offline, like the weights
     X0 = bf16(wl.X_bits)
     ws = w.decode_workspace(M, N, K, dev)
     wp_bytes = Wp0.data.numel()
@@ -226,7 +227,7 @@ def run_decode(args, torch, w, wl, dev):
 
     def step(i):
         st = sets[i % nsets]
-        w.w4a4_decode(st["X"], A, B, rh, rl, st["Wp"], ws, out=st["Y"])
+        w.w4a4_decode(st["X"], A, B, rh, rl, st["Wp"], ws, out=st["Y"], factors=fac)
 
     steps = args.steps
     if args.graph:
@@ -278,14 +279,14 @@ def run_decode(args, torch, w, wl, dev):
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), W {N}x{K} bf16 "
-                        f"N(0,0.02) prepared and packed offline; step = one fused decode launch pair "
-                        f"({'graph replay' if args.graph else 'eager launches'})",
+                        f"N(0,0.02) prepared and packed offline, block transforms prepared offline; step = one "
+                        f"fused decode launch ({'graph replay' if args.graph else 'eager launches'})",
             "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets, "graph": args.graph,
             "factors": args.factors, "clip": not args.no_clip,
         },
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_partial_kernel + decode_reduce_kernel (one step)"},
+                     "kernel": "decode_fused_kernel (one launch per step)"},
         "kernels": {"decode_step": {"us": t_step * 1e6, "GB/s": gbs, "algorithmic_bytes": alg_bytes,
                                     "TFLOP/s": 2.0 * M * N * K / t_step / 1e12}},
         "cpu_baseline": None,

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BATQ_ABI_VERSION 2
+#define BATQ_ABI_VERSION 3
 
 typedef enum {
   BATQ_OK = 0,
@@ -241,35 +241,58 @@ batq_status batq_kv_cache_quant(const void* KV_bf16, int64_t T, int64_t HD, int6
  */
 #define BATQ_DECODE_MAX_M 32
 
-/* Workspace bytes batq_w4a4_decode needs for (M, N, K): fp32 partial tiles,
- * one per 256-column chunk, K split and token.  A split covers one 256-k stage
- * of K, or two when M > 16 and there are more than 256 (chunk, stage) pairs.
- * -1 for M outside [0, 32], N < 0 or K not a positive multiple of 256. */
+/* Workspace bytes batq_w4a4_decode needs for (M, N, K): 16 KiB of arrival
+ * counters, then fp32 partial tiles, one per 128-column chunk, K split and
+ * token, where a K split covers two 256-k stages; 0 when K is at most 512 (one
+ * split: Y is written directly, no workspace is touched).
+ * -1 for M outside [0, 32], N outside [0, 524288] or K not a positive
+ * multiple of 256. */
 int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Y[M][N] = deq(Q(X P)) deq(Wp)^T with the activation path fused into the
- * GEMM: the block transform, clip and MXFP4 quantisation of X (bit-identical
- * to batq_act_transform_quant) feed the block-scaled MFMA against weights
- * packed by batq_weight_pack inside one kernel, split over 256-column chunks
- * and ranges of K; a second, small launch sums the K ranges' fp32 partials in
- * a fixed order, so results are deterministic and within the fp32
- * accumulation bound of the unsplit product.
+ * GEMM, in one launch: the block transform, clip and MXFP4 quantisation of X
+ * (bit-identical to batq_act_transform_quant) feed the block-scaled MFMA
+ * against weights packed by batq_weight_pack, split over 128-column chunks and
+ * K splits of two 256-k stages.  Each split's fp32 partial tile goes to the
+ * workspace; the workgroup that finishes a chunk last adds the chunk's
+ * partials in split order and writes Y, so results are deterministic and
+ * within the fp32 accumulation bound of the unsplit product.
  * X_bf16: [M][ldx] bf16, 1 <= M <= 32 (M == 0 or N == 0 is a no-op), K a
  * multiple of 256, ldx >= K and a multiple of 8, X 16-byte aligned.  A, B,
  * r_hi, r_lo: as for batq_act_transform_quant (ratios may both be NULL: no
- * clipping).  Wp: packed weights for (N, K), 16-byte aligned.  Y: [M][N] bf16
+ * clipping).  factors: NULL, or the block transforms prepared from the same
+ * A and B by batq_decode_prepare_factors (16-byte aligned; faster, same
+ * results).  Wp: packed weights for (N, K), 16-byte aligned.  Y: [M][N] bf16
  * or float, 4-byte aligned.  Xq [M][K/2] (8-byte aligned) and Xs [M][K/32]:
  * optional, both NULL or both set; when set they also receive the quantised
  * activations.  workspace: device memory of at least
  * batq_decode_workspace_bytes(M, N, K) bytes, 256-byte aligned, owned by the
- * caller, any contents (the call overwrites what it reads).  Calls that share
- * a workspace must not overlap (use one stream).
+ * caller.  Its first 16 KiB (the arrival counters) must be zero before the
+ * workspace's first use (allocate it zeroed); every call leaves them zero
+ * again.  The rest may hold anything (the call writes what it reads).  Calls
+ * that share a workspace must not overlap (use one stream).
  * Errors: SHAPE (also a workspace that is too small), NULL, ALIGN,
  * UNSUPPORTED (factor size or output type), HIP. */
 batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                             const float* A, const float* B, const float* r_hi, const float* r_lo,
-                             const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq, uint8_t* Xs,
-                             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                             const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                             const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
+                             uint8_t* Xq, uint8_t* Xs, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Bytes of the prepared block transforms of a K-channel layer for the decode
+ * step: K/32 x 6144.  -1 for K not a positive multiple of 256.  Host only. */
+int64_t batq_decode_factors_bytes(int64_t K);
+
+/* Offline, once per layer (like the weights): the decode step's block
+ * transforms P_i = B_i (x) A prepared as the exact three-way bf16 split of
+ * P_i^T in the matrix-core operand order, the same bits the decode kernel
+ * would build from A and B_i [en.papernotes.org, Key Designs §2: one shared
+ * A, a private B_i per block].  Passed as `factors` to the decode calls, it
+ * replaces the per-call rebuild of every P_i (results identical bit for bit).
+ * A: [a][a], B: [K/32][b][b] float (device); factors: batq_decode_factors_bytes(K)
+ * bytes, 16-byte aligned.  Errors: SHAPE, UNSUPPORTED, NULL, ALIGN, HIP. */
+batq_status batq_decode_prepare_factors(int64_t K, int32_t a, int32_t b, const float* A, const float* B,
+                                        uint8_t* factors, hipStream_t stream);
 
 /* ------------------------------------------------ fused decode, no allocation
  * For callers that cannot allocate device memory or pass a workspace: code
@@ -288,17 +311,17 @@ int64_t batq_decode_noalloc_scratch_bytes(void);
  * call on a device looks up that device's copy of the array
  * (hipGetSymbolAddress, with the device current; the device of the calling
  * thread must be the stream's device, as for any launch) and keeps its
- * address; each GPU holds its copy until the process ends.  Every call on a
- * GPU shares that GPU's array and overwrites what it reads, so nothing needs
- * clearing between calls, but calls that overlap on one GPU (other streams,
- * other threads) race: serialise them.  The array keeps the last call's
- * partials.
+ * address; each GPU holds its copy until the process ends.  The array starts
+ * zeroed (its arrival counters must), and every call leaves the counters zero
+ * and overwrites the partials it reads, so nothing needs clearing between
+ * calls; calls that overlap on one GPU (other streams, other threads) race:
+ * serialise them.  The array keeps the last call's partials.
  * Errors: as batq_w4a4_decode; TOO_LARGE (see above); HIP (also the address
  * lookup failing). */
 batq_status batq_w4a4_decode_noalloc(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                                     const float* A, const float* B, const float* r_hi, const float* r_lo,
-                                     const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq,
-                                     uint8_t* Xs, hipStream_t stream);
+                                     const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                                     const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
+                                     uint8_t* Xq, uint8_t* Xs, hipStream_t stream);
 
 #ifdef __cplusplus
 }

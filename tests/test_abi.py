@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.batq_abi_version() == 2
+    assert lib.batq_abi_version() == 3
     for s in range(8):
         assert lib.batq_status_str(s) and lib.batq_status_str(s) != b"unknown status"
     assert lib.batq_status_str(99) == b"unknown status"
@@ -153,22 +153,27 @@ def test_packed_gemm_kernel_choice(lib):
 
 
 def test_decode_workspace_bytes(lib):
+    """16 KiB of arrival counters, then fp32 partial tiles: one per 128-column
+    chunk, K split of two 256-k stages and token; none when K is a single
+    split (Y is written directly)."""
     f = lib.batq_decode_workspace_bytes
-    assert f(16, 4096, 4096) == 16 * 16 * 16 * 256 * 4      # one stage per K split
-    assert f(1, 300, 512) == 2 * 2 * 1 * 256 * 4
-    assert f(4, 12288, 4096) == 48 * 16 * 4 * 256 * 4       # up to 16 tokens: one stage per split
-    assert f(8, 12288, 12288) == 48 * 48 * 8 * 256 * 4
-    assert f(32, 4096, 4096) == 16 * 16 * 32 * 256 * 4      # 256 workgroups: one stage
-    assert f(32, 12288, 4096) == 48 * 8 * 32 * 256 * 4      # more: two stages per split
-    assert f(17, 4096, 12288) == 16 * 24 * 17 * 256 * 4
+    C = 16384
+    assert f(16, 4096, 4096) == C + 32 * 8 * 16 * 128 * 4    # 8 splits of 2 stages
+    assert f(1, 300, 512) == 0                                # 2 stages: one split
+    assert f(4, 12288, 4096) == C + 96 * 8 * 4 * 128 * 4
+    assert f(8, 12288, 12288) == C + 96 * 24 * 8 * 128 * 4
+    assert f(32, 4096, 4096) == C + 32 * 8 * 32 * 128 * 4
+    assert f(17, 4096, 12288) == C + 32 * 24 * 17 * 128 * 4
+    assert f(3, 100, 1280) == C + 1 * 3 * 3 * 128 * 4        # 5 stages: splits of 2, 2 and 1
+    assert f(1, 524288, 1024) == C + 4096 * 2 * 1 * 128 * 4 and f(1, 524289, 1024) == -1
     assert f(0, 256, 256) == 0
     assert f(33, 256, 256) == -1 and f(-1, 256, 256) == -1
     assert f(4, 256, 100) == -1 and f(4, 256, 0) == -1 and f(4, -1, 256) == -1
 
 
-def _dec(lib, x=FAKE, M=4, K=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0, wp=FAKE, N=256, y=FAKE, out=0,
+def _dec(lib, x=FAKE, M=4, K=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, fa=0, rh=0, rl=0, wp=FAKE, N=256, y=FAKE, out=0,
          xq=0, xs=0, ws=FAKE, wsb=1 << 30):
-    return lib.batq_w4a4_decode(x, M, K, ld, a, b, A, B, rh, rl, wp, N, y, out, xq, xs, ws, wsb, None)
+    return lib.batq_w4a4_decode(x, M, K, ld, a, b, A, B, fa, rh, rl, wp, N, y, out, xq, xs, ws, wsb, None)
 
 
 def test_decode_argument_checks(lib):
@@ -191,6 +196,7 @@ def test_decode_argument_checks(lib):
     assert _dec(lib, y=FAKE + 2) == ALIGN
     assert _dec(lib, ws=FAKE + 16) == ALIGN
     assert _dec(lib, xq=FAKE + 4, xs=FAKE) == ALIGN
+    assert _dec(lib, fa=FAKE + 8) == ALIGN
     # empty batch or no columns: no-ops that return before touching the GPU
     assert _dec(lib, M=0) == OK
     assert _dec(lib, N=0) == OK
@@ -277,3 +283,15 @@ def test_probe_argument_checks(lib):
     assert lib.batq_probe_hbm_stream(FAKE, g, FAKE, 3, None) == UNSUP
     assert lib.batq_probe_hbm_stream(FAKE, g - 16, FAKE, 4, None) == SHAPE
     assert lib.batq_probe_hbm_stream(FAKE, g, 0, 4, None) == NULL
+
+
+def test_decode_prepared_factor_checks(lib):
+    assert lib.batq_decode_factors_bytes(4096) == 128 * 6144
+    assert lib.batq_decode_factors_bytes(4000) == -1 and lib.batq_decode_factors_bytes(0) == -1
+    f = lib.batq_decode_prepare_factors
+    assert f(4000, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(4096, 8, 8, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(4096, 3, 32 // 3, FAKE, FAKE, FAKE, None) in (SHAPE, UNSUP)
+    assert f(4096, 8, 4, 0, FAKE, FAKE, None) == NULL
+    assert f(4096, 8, 4, FAKE, FAKE, 0, None) == NULL
+    assert f(4096, 8, 4, FAKE, FAKE, FAKE + 4, None) == ALIGN

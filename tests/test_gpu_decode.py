@@ -72,10 +72,13 @@ def test_decode_codes_match_oracle_and_transform_kernel(w, M, K, N, a, seed):
     parity.compare_quant(xq.cpu().numpy(), xs.cpu().numpy(), dec, label=f"decode {M}x{K}")
 
 
-# The last two shapes split K two stages per workgroup (more than 16 tokens
-# and more than 256 workgroups); the others one.
+# K splits of two 256-k stages: the first shape is one split (Y written
+# directly), 1024 is two, 1280 ends in a split of one stage, the others are 6
+# to 24 splits added by the last-arriving workgroup of each chunk; N covers
+# partial 128-column chunks.
 @pytest.mark.parametrize("M,K,N,seed", [(1, 256, 256, 11), (7, 1024, 300, 12), (16, 4096, 4096, 13),
-                                        (32, 3072, 777, 14), (32, 4096, 12288, 15), (17, 12288, 4096, 16)])
+                                        (32, 3072, 777, 14), (32, 4096, 12288, 15), (17, 12288, 4096, 16),
+                                        (9, 1280, 200, 17)])
 def test_decode_gemm_exact_operands(w, M, K, N, seed):
     """Identity factors, no clipping and activations that are exact MXFP4 values
     (every block holds a +-6 code): the quantisation has no free decision, so
@@ -109,9 +112,13 @@ def test_decode_gemm_exact_operands(w, M, K, N, seed):
     assert np.array_equal(Yb.float().cpu().numpy(), parity.bf16_rne(Y.cpu().numpy()))
 
 
+COUNTER_BYTES = 16384  # the workspace's leading arrival counters
+
+
 def test_decode_deterministic_and_reusable_workspace(w):
-    """Two calls on one workspace, the first over a workspace full of junk,
-    give the same bits (the K splits are summed in a fixed order)."""
+    """Two calls on one workspace, the first over partial tiles full of junk
+    (zero arrival counters), give the same bits (the K splits are summed in a
+    fixed order), and each call leaves the counters at zero."""
     note("case: decode determinism")
     wl = gen.make_workload(4)
     wq, wsc = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
@@ -119,24 +126,29 @@ def test_decode_deterministic_and_reusable_workspace(w):
     M, K = wl.X_bits.shape
     ws = w.decode_workspace(M, Wp.N, K, DEV)
     ws.fill_(0xA5)
+    ws[:COUNTER_BYTES].zero_()
     args = (dev_bf16(wl.X_bits), dev_f32(wl.A), dev_f32(wl.B), dev_f32(w.clip_ratios(wl.alpha)),
             dev_f32(w.clip_ratios(wl.beta)), Wp, ws)
     y1 = w.w4a4_decode(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
     y2 = w.w4a4_decode(*args, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
 
 
 def test_decode_workspace_reused_across_shapes(w):
-    """One workspace, sized for the largest call and filled with junk, serves
-    calls of different M, N and K in turn (each call's partial area overlaps
-    the earlier calls' data); each matches a call on a fresh workspace bit for
-    bit."""
+    """One workspace, sized for the largest call, with junk past its zeroed
+    counters, serves calls of different M, N and K in turn (each call's
+    partial area overlaps the earlier calls' data); each matches a call on a
+    fresh workspace bit for bit."""
     note("case: decode workspace reuse across shapes")
     rng = np.random.default_rng(7)
     shapes = [(32, 12288, 4096), (3, 300, 512), (16, 4096, 12288), (1, 8192, 256), (32, 12288, 4096)]
     big = max(w.decode_workspace_bytes(M, N, K) for M, N, K in shapes)
     ws = torch.full((big,), 0x5A, dtype=torch.uint8, device=DEV)
+    ws[:COUNTER_BYTES].zero_()
     for M, N, K in shapes:
         note(f"  shape M={M} N={N} K={K}")
         Wq = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).to(DEV)
@@ -215,3 +227,30 @@ def test_decode_graph_replays_match_eager(w):
         assert torch.equal(Y.view(torch.int32), eager.view(torch.int32)), rep
         w.w4a4_decode(other, A, B, rh, rl, Wp, ws2, out_dtype=torch.float32)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("a,M,K,N", [(1, 3, 512, 200), (2, 16, 1024, 300), (4, 9, 1280, 260), (8, 16, 4096, 4096),
+                                     (16, 32, 2048, 520), (32, 5, 768, 128)])
+def test_decode_prepared_factors_equal_built_ones(w, a, M, K, N):
+    """Block transforms prepared once (batq_decode_prepare_factors) give the
+    same bits as the ones the kernel builds from A and B_i: Y and the
+    quantised activations, for every shared-factor size."""
+    note(f"case: decode prepared factors a={a} {M}x{K} N={N}")
+    wl = gen.make_custom(M, K, N, a=a, seed=100 + a)
+    wq, wsc = w.prepare_weight(dev_bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    Wp = w.weight_pack(wq, wsc)
+    A, B = dev_f32(wl.A), dev_f32(wl.B)
+    rh, rl = dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta))
+    X = dev_bf16(wl.X_bits)
+    fac = w.decode_prepare_factors(A, B, K)
+    outs = []
+    for f in (None, fac):
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+        xs = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+        y = w.w4a4_decode(X, A, B, rh, rl, Wp, w.decode_workspace(M, N, K, DEV), out_dtype=torch.float32,
+                          quantized_out=(xq, xs), factors=f)
+        outs.append((y, xq, xs))
+    torch.cuda.synchronize()
+    (y0, q0, s0), (y1, q1, s1) = outs
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    assert torch.equal(q0, q1) and torch.equal(s0, s1)

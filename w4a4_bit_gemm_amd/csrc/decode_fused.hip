@@ -4,25 +4,30 @@
 // A Worked Example: transform block by block, clip, quantise, multiply].
 //
 // At decode sizes a separate transform launch is pure latency, and a GEMM
-// tiled over M cannot keep enough weight bytes in flight.  So the work is
-// split over (256-column chunk c, K split sp of SPW 256-k stages):
-//
-// decode_partial_kernel, one workgroup per (c, sp):
-//   1. every wave requests its weight records (its 64 columns, SPW stages)
-//      before the transform, so that HBM latency overlaps it.  A wave's loads
-//      complete in issue order, so with one stage per workgroup the wave's
-//      activation-side loads (factor entries, token rows, ratios) go out just
-//      before the weights: the transform then waits only for them.  With
-//      more stages their registers would not fit, and they follow the weights;
-//   2. the workgroup transforms and quantises the split's activation blocks
-//      for all tokens with the same per-block arithmetic as the transform
-//      kernel (block_quant.h): the codes are identical bit for bit.  They are
-//      staged in LDS in the MFMA operand order;
-//   3. each wave multiplies them with its weights on the block-scaled MFMA,
-//      stage by stage in one accumulator, and stores the fp32 partial tile.
-// decode_reduce_kernel then sums the splits of every output in split order
-// (deterministic) and writes Y.  The launch boundary orders the two, so no
-// workgroup ever waits for or synchronises with another.
+// tiled over M cannot keep enough weight bytes in flight.  So one launch
+// splits the work over (128-column chunk c, K split sp of up to kSplitStages
+// 256-k stages), one workgroup of 8 waves each:
+//   1. wave w requests the activation-side inputs of block w of each stage of
+//      the split (factor entries, the tokens' channels, ratios), then its
+//      weight record: 32-column group w % 4 of stage w / 4.  A wave's loads
+//      complete in issue order, so the transform waits only for the
+//      activation side while the weight bytes stream in behind it;
+//   2. wave w transforms and quantises its blocks for all tokens with the
+//      same per-block arithmetic as the transform kernel (block_quant.h): the
+//      codes are identical bit for bit.  They are staged in LDS in the MFMA
+//      operand order;
+//   3. wave w multiplies its stage's codes with its weight record on the
+//      block-scaled MFMA; the two waves of a column group add their
+//      accumulators in stage order through LDS;
+//   4. with one split the result is Y.  Otherwise each workgroup writes its
+//      fp32 partial tile with device-scope stores (they go to the coherence
+//      point, past this XCD's L2), waits until they are acknowledged, and
+//      counts itself on its chunk's counter with one device-scope atomic.
+//      The workgroup that arrives last reads the chunk's partials with
+//      device-scope loads, adds them in split order and writes Y, then
+//      returns the counter to zero.  No workgroup ever waits for another;
+//      no cache-wide write-back or invalidation is needed; the sum is
+//      deterministic.
 #include <mutex>
 
 #include "block_quant.h"
@@ -41,7 +46,12 @@ constexpr int kMaxDevices = 64;
 std::mutex scratch_mu;
 void* scratch_ptr[kMaxDevices] = {};
 
-constexpr int kQRow = 144;  // staged code row: 8 blocks x 16 bytes + 16 pad (conflict-free reads)
+constexpr int kQRow = 144;        // staged code row: 8 blocks x 16 bytes + 16 pad (conflict-free reads)
+constexpr int kSplitStages = 2;   // 256-k stages per K split
+constexpr int kChunkCols = 128;   // columns per workgroup: four 32-column groups
+constexpr int kDecWaves = 8;      // one block of each stage per wave; one (group, stage) product per wave
+constexpr int kGroups = kChunkCols / 32;
+static_assert(kGroups * kSplitStages == kDecWaves, "one (column group, stage) product per wave");
 
 template <int J>
 __device__ __forceinline__ f32x16 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb, f32x16 acc) {
@@ -61,6 +71,26 @@ __device__ __forceinline__ uint32_t ld4_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
+// Factor entries behind lane (j, h)'s part of P_i^T for a compile-time shared
+// size 2^LA: P_i[k][j] = Bi[k >> LA][j >> LA] * A[k % a][j % a]; entries that
+// coincide are loaded once (10 loads at a = 8 instead of 32).
+template <int LA>
+__device__ __forceinline__ PFactors load_p_factors_la(const float* __restrict__ A, const float* __restrict__ Bi,
+                                                      int j, int h) {
+  constexpr int a = 1 << LA;
+  constexpr int bdim = 32 >> LA;
+  PFactors f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int k = 16 * ks + 8 * h + t;
+      f.bv[ks][t] = Bi[(k >> LA) * bdim + (j >> LA)];
+      f.av[ks][t] = A[(k & (a - 1)) * a + (j & (a - 1))];
+    }
+  return f;
+}
+
 // Inputs of one activation block for the wave's 32 token slots: factor
 // entries, the lane's 16 channels of token j (zero for j >= M), the ratios.
 struct ActIn {
@@ -68,25 +98,68 @@ struct ActIn {
   uint4 x0, x1;
   float rh, rl;
 };
+// Every load is unconditional (rows past M read row M - 1 and are zeroed
+// after), so that no branch separates the loads: the compiler's wait for
+// them then counts exactly the loads issued later, the weights' included.
+template <int LA>
 __device__ __forceinline__ ActIn load_act(const DecodeArgs& p, int64_t blk, int j, int h) {
-  const int bdim = 32 >> p.a_log2;
+  constexpr int bdim = 32 >> LA;
   ActIn in;
-  in.f = load_p_factors(p.A, p.B + blk * bdim * bdim, p.a_log2, j, h);
-  in.x0 = in.x1 = make_uint4(0, 0, 0, 0);
-  if (j < p.M) {
-    const uint16_t* xr = p.x + (int64_t)j * p.ldx + blk * 32 + 8 * h;
-    in.x0 = *reinterpret_cast<const uint4*>(xr);
-    in.x1 = *reinterpret_cast<const uint4*>(xr + 16);
-  }
+  in.f = load_p_factors_la<LA>(p.A, p.B + blk * bdim * bdim, j, h);
+  const int64_t row = j < p.M ? j : p.M - 1;
+  const uint16_t* xr = p.x + row * p.ldx + blk * 32 + 8 * h;
+  in.x0 = *reinterpret_cast<const uint4*>(xr);
+  in.x1 = *reinterpret_cast<const uint4*>(xr + 16);
   in.rh = p.r_hi ? p.r_hi[blk] : 1.0f;
   in.rl = p.r_lo ? p.r_lo[blk] : 1.0f;
   return in;
 }
+// The tokens' channels and the ratios only (prepared transforms).
+__device__ __forceinline__ ActIn load_x_ratios(const DecodeArgs& p, int64_t blk, int j, int h) {
+  ActIn in;
+  const int64_t row = j < p.M ? j : p.M - 1;
+  const uint16_t* xr = p.x + row * p.ldx + blk * 32 + 8 * h;
+  in.x0 = *reinterpret_cast<const uint4*>(xr);
+  in.x1 = *reinterpret_cast<const uint4*>(xr + 16);
+  in.rh = p.r_hi ? p.r_hi[blk] : 1.0f;
+  in.rl = p.r_lo ? p.r_lo[blk] : 1.0f;
+  return in;
+}
+// Prepared split of block blk: parts hi[0], hi[1], mid[0], mid[1], lo[0],
+// lo[1], each 64 lanes x 16 bytes.
+__device__ __forceinline__ PSplit load_prepared(const uint8_t* __restrict__ pp, int64_t blk, int lane) {
+  const uint8_t* b = pp + blk * kDecodeFactorBlockBytes + 16 * lane;
+  PSplit ps;
+  ps.hi[0] = ld16(b);
+  ps.hi[1] = ld16(b + 1024);
+  ps.mid[0] = ld16(b + 2048);
+  ps.mid[1] = ld16(b + 3072);
+  ps.lo[0] = ld16(b + 4096);
+  ps.lo[1] = ld16(b + 5120);
+  return ps;
+}
+__device__ __forceinline__ uint4 zero_unless(bool keep, uint4 v) {
+  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
 
-template <int SPW>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int nchunk, int nsplit) {
-  __shared__ __attribute__((aligned(16))) uint8_t qs[SPW][32 * kQRow];
-  __shared__ __attribute__((aligned(16))) uint8_t ss[SPW][32 * 8];
+// Output element of a 32-row x 32-column MFMA tile: lane (r32, g), register r
+// holds row 8 (r / 4) + 4 g + r % 4 of column r32.
+__device__ __forceinline__ int tile_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// Bytes of the per-chunk arrival counters at the start of the workspace: a
+// fixed region, so that calls of any shape find their counters where earlier
+// calls left them at zero (never under an earlier call's partials).
+__host__ __device__ constexpr int64_t counter_bytes(int64_t) { return kDecodeCounterBytes; }
+
+// PREP: the split of each P_i comes prepared (6 coalesced loads per block)
+// instead of being built from the factors (10 loads and ~140 vector
+// instructions per block, repeated by every workgroup of a K split).
+template <int LA, bool PREP>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_fused_kernel(DecodeArgs p, int nchunk, int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kSplitStages][32 * kQRow];
+  __shared__ __attribute__((aligned(16))) uint8_t ss[kSplitStages][32 * 8];
+  __shared__ __attribute__((aligned(16))) float red[kDecWaves - kGroups][16 * 64];
+  __shared__ int last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,167 +167,206 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs p, int n
   const int c = blockIdx.x % nchunk;
   const int sp = blockIdx.x / nchunk;
   const int64_t nst = p.K / 256;
-  const int64_t s0 = (int64_t)sp * SPW;
-
-  // Wave w quantises blocks w and w + 4 of every stage of the split for
-  // tokens 0..31 (rows >= M are zero and never stored).
+  const int64_t s0 = (int64_t)sp * kSplitStages;
+  const int nstage = (int)(nst - s0 < kSplitStages ? nst - s0 : kSplitStages);  // stages of this split
   const int j = lane & 31;
   const int h = lane >> 5;
-  ActIn pre[2];
-  if constexpr (SPW == 1) {
-    if (s0 < nst) {
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb) pre[bb] = load_act(p, s0 * 8 + wave + 4 * bb, j, h);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
-  // 1. weight records of this wave's two 32-column groups for the split's
-  // stages (stages past K are never requested).
-  const int64_t n0 = (int64_t)c * 256 + 64 * wave;
+  // 1. activation side of block `wave` of every stage, then the weights.
+  ActIn in[kSplitStages];
+  PSplit pre[kSplitStages];
+#pragma unroll
+  for (int t = 0; t < kSplitStages; ++t) {  // a stage past the split's end reloads its last one (unused)
+    const int64_t blk = (s0 + (t < nstage ? t : nstage - 1)) * 8 + wave;
+    if constexpr (PREP) {
+      in[t] = load_x_ratios(p, blk, j, h);
+      pre[t] = load_prepared(p.pprep, blk, lane);
+    } else {
+      in[t] = load_act<LA>(p, blk, j, h);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int gsel = wave % kGroups;  // 32-column group within the chunk
+  const int tsel = wave / kGroups;  // stage of the split whose product this wave forms
   const int64_t n32_max = (p.N + 31) / 32;
-  const int64_t g0 = n0 / 32 < n32_max ? n0 / 32 : n32_max - 1;  // clamped groups are computed, never stored
-  const int64_t g1 = n0 / 32 + 1 < n32_max ? n0 / 32 + 1 : n32_max - 1;
-  uint4 b0[SPW][4], b1[SPW][4];
-  uint32_t bs0[SPW], bs1[SPW];
+  const int64_t gq = (int64_t)c * kGroups + gsel;
+  const int64_t g32 = gq < n32_max ? gq : n32_max - 1;  // a clamped group is computed, never stored
+  uint4 b[4];
+  {
+    const int tl = tsel < nstage ? tsel : nstage - 1;  // past the split's end: a valid record, unused
+    const uint8_t* r = p.wp + (g32 * nst + s0 + tl) * kPackGroupBytes + 16 * lane;
 #pragma unroll
-  for (int t = 0; t < SPW; ++t) {
-    if (s0 + t < nst) {
-      const uint8_t* r0 = p.wp + (g0 * nst + s0 + t) * kPackGroupBytes + 16 * lane;
-      const uint8_t* r1 = p.wp + (g1 * nst + s0 + t) * kPackGroupBytes + 16 * lane;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        b0[t][jj] = ld16_stream(r0 + 1024 * jj);
-        b1[t][jj] = ld16_stream(r1 + 1024 * jj);
-      }
-      bs0[t] = ld4_stream(r0 + 4096 - 12 * lane);
-      bs1[t] = ld4_stream(r1 + 4096 - 12 * lane);
-    }
+    for (int jj = 0; jj < 4; ++jj) b[jj] = ld16_stream(r + 1024 * jj);
   }
+  const uint32_t bsc = ld4_stream(p.wp + (g32 * nst + s0 + (tsel < nstage ? tsel : nstage - 1)) * kPackGroupBytes +
+                                  4096 + 4 * lane);
+  __builtin_amdgcn_sched_barrier(0);
 
-  if constexpr (SPW == 1) __builtin_amdgcn_sched_barrier(0);
-
-  // 2. activation blocks, staged in LDS in the MFMA operand order.
+  // 2. transform and quantise; codes staged in LDS in the MFMA operand order.
 #pragma unroll
-  for (int t = 0; t < SPW; ++t) {
-    if (s0 + t >= nst) break;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int lb = wave + 4 * bb;  // block within the stage
-      const int64_t blk = (s0 + t) * 8 + lb;
-      const ActIn in = SPW == 1 ? pre[bb] : load_act(p, blk, j, h);
-      const f32x16 acc = transform_block(split_p(in.f), in.x0, in.x1);
-      int sbyte;
-      const uint2 code = quant_block_e2m1(acc, in.rh, in.rl, h, sbyte);
-      *reinterpret_cast<uint2*>(&qs[t][j * kQRow + 16 * lb + 8 * h]) = code;
-      if (h == 0) ss[t][j * 8 + lb] = (uint8_t)sbyte;
-      if (p.xq != nullptr && c == 0 && j < p.M) {  // optional copy of the quantised activations
-        *reinterpret_cast<uint2*>(p.xq + (int64_t)j * (p.K >> 1) + blk * 16 + 8 * h) = code;
-        if (h == 0) p.xs[(int64_t)j * (p.K >> 5) + blk] = (uint8_t)sbyte;
-      }
+  for (int t = 0; t < kSplitStages; ++t) {
+    if (t >= nstage) break;
+    const int64_t blk = (s0 + t) * 8 + wave;
+    const PSplit ps = PREP ? pre[t] : split_p(in[t].f);
+    const f32x16 acc = transform_block(ps, zero_unless(j < p.M, in[t].x0), zero_unless(j < p.M, in[t].x1));
+    int sbyte;
+    const uint2 code = quant_block_e2m1(acc, in[t].rh, in[t].rl, h, sbyte);
+    *reinterpret_cast<uint2*>(&qs[t][j * kQRow + 16 * wave + 8 * h]) = code;
+    if (h == 0) ss[t][j * 8 + wave] = (uint8_t)sbyte;
+    if (p.xq != nullptr && c == 0 && j < p.M) {  // optional copy of the quantised activations
+      *reinterpret_cast<uint2*>(p.xq + (int64_t)j * (p.K >> 1) + blk * 16 + 8 * h) = code;
+      if (h == 0) p.xs[(int64_t)j * (p.K >> 5) + blk] = (uint8_t)sbyte;
     }
   }
   __syncthreads();
 
-  // 3. MMA: lane (r32, g) of sub-step jj carries block 4 g + jj of token r32
-  // (the packed weight record holds the matching blocks of its rows).
+  // 3. MMA of stage tsel against column group gsel: lane (r32, g) of sub-step
+  // jj carries block 4 g + jj of token r32 (the packed record holds the
+  // matching blocks of its rows).
   const int r32 = lane & 31;
   const int g = lane >> 5;
-  f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-  for (int t = 0; t < SPW; ++t) {
-    if (s0 + t >= nst) break;
-    const uint8_t* qrow = &qs[t][r32 * kQRow + 64 * g];
-    const uint32_t sa = ld4(&ss[t][r32 * 8 + 4 * g]);
-    const uint4 a0 = ld16(qrow), a1 = ld16(qrow + 16), a2 = ld16(qrow + 32), a3 = ld16(qrow + 48);
-    acc0 = mfma_fp4<0>(a0, b0[t][0], sa, bs0[t], acc0);
-    acc1 = mfma_fp4<0>(a0, b1[t][0], sa, bs1[t], acc1);
-    acc0 = mfma_fp4<1>(a1, b0[t][1], sa, bs0[t], acc0);
-    acc1 = mfma_fp4<1>(a1, b1[t][1], sa, bs1[t], acc1);
-    acc0 = mfma_fp4<2>(a2, b0[t][2], sa, bs0[t], acc0);
-    acc1 = mfma_fp4<2>(a2, b1[t][2], sa, bs1[t], acc1);
-    acc0 = mfma_fp4<3>(a3, b0[t][3], sa, bs0[t], acc0);
-    acc1 = mfma_fp4<3>(a3, b1[t][3], sa, bs1[t], acc1);
+  f32x16 acc = {};
+  if (tsel < nstage) {
+    const uint8_t* qrow = &qs[tsel][r32 * kQRow + 64 * g];
+    const uint32_t sa = ld4(&ss[tsel][r32 * 8 + 4 * g]);
+    acc = mfma_fp4<0>(ld16(qrow), b[0], sa, bsc, acc);
+    acc = mfma_fp4<1>(ld16(qrow + 16), b[1], sa, bsc, acc);
+    acc = mfma_fp4<2>(ld16(qrow + 32), b[2], sa, bsc, acc);
+    acc = mfma_fp4<3>(ld16(qrow + 48), b[3], sa, bsc, acc);
   }
-
-  // 4. partial tile [M][256] of (c, sp); lane (r32, g), register r holds row
-  // 8 (r / 4) + 4 g + r % 4 of columns 64 wave + r32 and 64 wave + 32 + r32.
-  const int64_t M = p.M;
-  float* part = p.part + ((int64_t)c * nsplit + sp) * M * 256;
+  // The waves of stage 1 hand their accumulators to the wave of stage 0 of
+  // their column group, which adds them in stage order.
+  if (wave >= kGroups) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-    if (row < M) {
-      part[row * 256 + 64 * wave + r32] = acc0[r];
-      part[row * 256 + 64 * wave + 32 + r32] = acc1[r];
+    for (int r = 0; r < 16; ++r) red[wave - kGroups][r * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  const int64_t M = p.M;
+  const int64_t col = (int64_t)c * kChunkCols + 32 * gsel + r32;
+  if (wave < kGroups) {
+    if (nstage > 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += red[wave][r * 64 + lane];
+    }
+    if (nsplit == 1) {  // 4. the whole K: this tile is Y
+      if (col < p.N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = tile_row(r, g);
+          if (row < M) {
+            if (p.out_f32)
+              reinterpret_cast<float*>(p.y)[row * p.N + col] = acc[r];
+            else
+              reinterpret_cast<uint16_t*>(p.y)[row * p.N + col] = (uint16_t)f32_to_bf16_rne(acc[r]);
+          }
+        }
+      }
+    } else {  // 4. the split's partial tile [M][kChunkCols], past this XCD's L2
+      float* part = p.part + counter_bytes(nchunk) / 4 + ((int64_t)c * nsplit + sp) * M * kChunkCols;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tile_row(r, g);
+        if (row < M)
+          __hip_atomic_store(part + row * kChunkCols + 32 * gsel + r32, acc[r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
-}
-
-// Y[row][4 q .. 4 q + 3 of chunk c] = sum of the splits' partials, in split
-// order; one (row, 4-column quad) per thread, all splits loaded together.
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p, int nchunk, int nsplit) {
-  const int64_t M = p.M;
-  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over nchunk x M x 64
-  if (item >= (int64_t)nchunk * M * 64) return;
-  const int64_t c = item / (M * 64);
-  const int64_t row = (item / 64) % M;
-  const int q = (int)(item % 64);
-  const float* pc = p.part + c * nsplit * M * 256 + row * 256 + 4 * q;
-  constexpr int kBatch = 16;
-  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-    float4 v[kBatch];
+  if (nsplit == 1) return;
+  // Every store of this workgroup is acknowledged before it counts itself.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  unsigned* cnt = reinterpret_cast<unsigned*>(p.part) + c;
+  if (tid == 0) {
+    const unsigned arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = arrived == (unsigned)(nsplit - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  // The last workgroup of chunk c: Y = the splits' partials added in split
+  // order, one (row, 4-column quad) per thread per pass.  The partials are
+  // read with device-scope buffer loads (cache-policy bit sc1: never served
+  // from a stale line of this XCD's L2), all of a thread's splits in flight
+  // at once.
+  const float* pc = p.part + counter_bytes(nchunk) / 4 + (int64_t)c * nsplit * M * kChunkCols;
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)pc, (short)0, (int)(nsplit * M * kChunkCols * 4), 0x00020000);
+  constexpr int kQuads = kChunkCols / 4;
+  constexpr int kSc1 = 1 << 4;  // buffer cache-policy bit: device scope
+  constexpr int kBatch = 8;
+  for (int64_t item = tid; item < M * kQuads; item += 64 * kDecWaves) {
+    const int64_t row = item / kQuads;
+    const int q = (int)(item % kQuads);
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int s0b = 0; s0b < nsplit; s0b += kBatch) {
+      f32x4 v[kBatch];
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t)
-      v[t] = s0 + t < nsplit ? *reinterpret_cast<const float4*>(pc + (int64_t)(s0 + t) * M * 256)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int t = 0; t < kBatch; ++t) {
+        const int sidx = s0b + t < nsplit ? s0b + t : nsplit - 1;  // in range; the extra ones are not added
+        v[t] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)((((int64_t)sidx * M + row) * kChunkCols + 4 * q) * 4),
+                                                     0, kSc1);
+      }
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      sum.x += v[t].x;
-      sum.y += v[t].y;
-      sum.z += v[t].z;
-      sum.w += v[t].w;
+      for (int t = 0; t < kBatch; ++t)
+        if (s0b + t < nsplit) sum += v[t];
+    }
+    const int64_t col0 = (int64_t)c * kChunkCols + 4 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t cc = col0 + e;
+      if (cc >= p.N) break;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.y)[row * p.N + cc] = sum[e];
+      else
+        reinterpret_cast<uint16_t*>(p.y)[row * p.N + cc] = (uint16_t)f32_to_bf16_rne(sum[e]);
     }
   }
-  const float out[4] = {sum.x, sum.y, sum.z, sum.w};
-  const int64_t col0 = c * 256 + 4 * q;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t col = col0 + e;
-    if (col >= p.N) break;
-    if (p.out_f32)
-      reinterpret_cast<float*>(p.y)[row * p.N + col] = out[e];
-    else
-      reinterpret_cast<uint16_t*>(p.y)[row * p.N + col] = (uint16_t)f32_to_bf16_rne(out[e]);
-  }
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 }
 
-// Stages per workgroup: one (the most workgroups, and each wave's activation
-// loads go out ahead of its weights) unless the fp32 partials would rival the
-// weights in bytes, i.e. above 16 tokens on grids of more than one workgroup
-// per CU: then two.  Measured on 1-32 tokens with K, N in {4096, 12288}: one
-// stage is 10-40 % faster up to 16 tokens; at 32 tokens two are 5-7 % faster
-// once there are more than 256 workgroups, and equal or slower below.
-int stages_per_wg(int64_t M, int64_t nchunk, int64_t nst) {
-  return (M <= 16 || nchunk * nst <= 256) ? 1 : 2;
-}
-
-template <int SPW>
+template <int LA>
 hipError_t launch_t(const DecodeArgs& a, int nchunk, int nsplit, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_partial_kernel<SPW>, dim3(nchunk * nsplit), dim3(256), 0, stream, a, nchunk, nsplit);
-  const int64_t items = (int64_t)nchunk * a.M * 64;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a, nchunk,
-                     nsplit);
+  if (a.pprep != nullptr)
+    hipLaunchKernelGGL((decode_fused_kernel<LA, true>), dim3(nchunk * nsplit), dim3(64 * kDecWaves), 0, stream, a,
+                       nchunk, nsplit);
+  else
+    hipLaunchKernelGGL((decode_fused_kernel<LA, false>), dim3(nchunk * nsplit), dim3(64 * kDecWaves), 0, stream, a,
+                       nchunk, nsplit);
   return hipGetLastError();
+}
+
+// One wave per block: the split the decode kernel would build, stored in
+// the prepared layout.
+__global__ __launch_bounds__(256) void decode_prepare_factors_kernel(const float* A, const float* B, int64_t nb,
+                                                                     int la, uint8_t* out) {
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nb) return;
+  const int lane = threadIdx.x & 63;
+  const int bdim = 32 >> la;
+  const PSplit ps = split_p(load_p_factors(A, B + blk * bdim * bdim, la, lane & 31, lane >> 5));
+  uint4* o = reinterpret_cast<uint4*>(out + blk * kDecodeFactorBlockBytes) + lane;
+  o[0] = ps.hi[0];
+  o[64] = ps.hi[1];
+  o[128] = ps.mid[0];
+  o[192] = ps.mid[1];
+  o[256] = ps.lo[0];
+  o[320] = ps.lo[1];
 }
 
 }  // namespace
 
 int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int64_t nchunk = (N + 255) / 256, nst = K / 256;
-  const int spw = stages_per_wg(M, nchunk, nst);
-  return nchunk * ((nst + spw - 1) / spw) * M * 256 * 4;
+  const int64_t nchunk = (N + kChunkCols - 1) / kChunkCols, nst = K / 256;
+  const int64_t nsplit = (nst + kSplitStages - 1) / kSplitStages;
+  return nsplit > 1 ? counter_bytes(nchunk) + nchunk * nsplit * M * kChunkCols * 4 : 0;
+}
+
+hipError_t launch_decode_prepare_factors(const float* A, const float* B, int64_t K, int a_log2, uint8_t* out,
+                                         hipStream_t stream) {
+  const int64_t nb = K / 32;
+  hipLaunchKernelGGL(decode_prepare_factors_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, A, B, nb,
+                     a_log2, out);
+  return hipGetLastError();
 }
 
 hipError_t decode_scratch(void** ptr) {
@@ -274,10 +386,16 @@ hipError_t decode_scratch(void** ptr) {
 }
 
 hipError_t launch_decode_fused(const DecodeArgs& args, hipStream_t stream) {
-  const int64_t nchunk = (args.N + 255) / 256, nst = args.K / 256;
-  const int spw = stages_per_wg(args.M, nchunk, nst);
-  const int nsplit = (int)((nst + spw - 1) / spw);
-  return spw == 2 ? launch_t<2>(args, (int)nchunk, nsplit, stream) : launch_t<1>(args, (int)nchunk, nsplit, stream);
+  const int64_t nchunk = (args.N + kChunkCols - 1) / kChunkCols, nst = args.K / 256;
+  const int nsplit = (int)((nst + kSplitStages - 1) / kSplitStages);
+  switch (args.a_log2) {
+    case 0: return launch_t<0>(args, (int)nchunk, nsplit, stream);
+    case 1: return launch_t<1>(args, (int)nchunk, nsplit, stream);
+    case 2: return launch_t<2>(args, (int)nchunk, nsplit, stream);
+    case 3: return launch_t<3>(args, (int)nchunk, nsplit, stream);
+    case 4: return launch_t<4>(args, (int)nchunk, nsplit, stream);
+    default: return launch_t<5>(args, (int)nchunk, nsplit, stream);
+  }
 }
 
 }  // namespace batq
