@@ -190,11 +190,11 @@ def cpu_baseline(wl, min_seconds: float, fmt: str = "e2m1", max_rows: int = 1024
 
 
 def run_decode(args, torch, w, wl, dev):
-    """The fused decode step: one w4a4_decode call (the activation transform,
-    clip and MXFP4 quantisation run inside the GEMM kernel; a second small
-    launch sums its K splits).  Bound: HBM (the packed weights are read once
-    per step).  Buffers rotate over enough sets that every step reads its
-    weights from HBM."""
+    """The fused decode step: one w4a4_decode call, one launch (the activation
+    transform, clip and MXFP4 quantisation run inside the GEMM kernel, and the
+    last workgroup of each column chunk sums its K splits).  Bound: HBM (the
+    packed weights are read once per step).  Buffers rotate over enough sets
+    that every step reads its weights from HBM."""
     M, K, N = wl.M, wl.K, wl.N
     if M > w.DECODE_MAX_M:
         print(f"--decode needs M <= {w.DECODE_MAX_M} (config 4); config {args.config} has M = {M}", file=sys.stderr)
@@ -263,6 +263,7 @@ def run_decode(args, torch, w, wl, dev):
     wall = time.perf_counter() - t0
     t_step = e0.elapsed_time(e1) * 1e-3 / steps  # GPU time per step, events on the launch stream
     alg_bytes = M * K * 2 + wp_bytes + M * N * 2  # X read, packed weights read, Y written
+    dec_kernel = f"decode_fused_kernel<{int(wl.a).bit_length() - 1},true>"  # log2 a, prepared block transforms
     gbs = alg_bytes / t_step / 1e9
     out = {
         "metric": METRIC_DECODE,
@@ -285,8 +286,8 @@ def run_decode(args, torch, w, wl, dev):
             "factors": args.factors, "clip": not args.no_clip,
         },
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_fused_kernel (one launch per step)"},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("decode_fused.hip", dec_kernel, wl.name),
+                     "kernel": dec_kernel},
         "kernels": {"decode_step": {"us": t_step * 1e6, "GB/s": gbs, "algorithmic_bytes": alg_bytes,
                                     "TFLOP/s": 2.0 * M * N * K / t_step / 1e12}},
         "cpu_baseline": None,
@@ -425,7 +426,8 @@ def measure_ceilings(torch, w, dev, act_read_bytes=None, act_write_ratio=4):
         # shader-clock cycles per 100 MHz real-time tick, over every wave of the last launch
         mf[f"{name}_clock_MHz"] = float(c[:, 0].sum() / c[:, 1].sum() * 100.0)
     gran = w.probe_stream_granule()
-    nbytes = 32 * gran  # 2 GiB
+    nbytes = (2 << 30) // gran * gran  # 2 GiB
+    assert nbytes == 2 << 30, gran
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     rsink = torch.empty(2048, dtype=torch.int32, device=dev)
     csrc = src[: nbytes // 8]
