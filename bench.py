@@ -215,7 +215,6 @@ def run_decode(args, torch, w, wl, dev):
     rl = None if args.no_clip else f32(w.clip_ratios(wl.beta))
     Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)  # offline
     Wp0 = w.weight_pack(Wq0, Ws0)
-    fac = w.decode_prepare_factors(A, B, K)  # offline, like the weights
     X0 = bf16(wl.X_bits)
     ws = w.decode_workspace(M, N, K, dev)
     wp_bytes = Wp0.data.numel()
@@ -227,7 +226,7 @@ def run_decode(args, torch, w, wl, dev):
 
     def step(i):
         st = sets[i % nsets]
-        w.w4a4_decode(st["X"], A, B, rh, rl, st["Wp"], ws, out=st["Y"], factors=fac)
+        w.w4a4_decode(st["X"], A, B, rh, rl, st["Wp"], ws, out=st["Y"])
 
     steps = args.steps
     if args.graph:
@@ -263,7 +262,7 @@ def run_decode(args, torch, w, wl, dev):
     wall = time.perf_counter() - t0
     t_step = e0.elapsed_time(e1) * 1e-3 / steps  # GPU time per step, events on the launch stream
     alg_bytes = M * K * 2 + wp_bytes + M * N * 2  # X read, packed weights read, Y written
-    dec_kernel = f"decode_fused_kernel<{int(wl.a).bit_length() - 1},true>"  # log2 a, prepared block transforms
+    dec_kernel = f"decode_fused_kernel<{int(wl.a).bit_length() - 1}>"  # log2 a
     gbs = alg_bytes / t_step / 1e9
     out = {
         "metric": METRIC_DECODE,
@@ -280,7 +279,7 @@ def run_decode(args, torch, w, wl, dev):
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: X {M}x{K} bf16 ({wl.meta['x_kind']}, {wl.meta['outliers']}), W {N}x{K} bf16 "
-                        f"N(0,0.02) prepared and packed offline, block transforms prepared offline; step = one "
+                        f"N(0,0.02) prepared and packed offline; step = one "
                         f"fused decode launch ({'graph replay' if args.graph else 'eager launches'})",
             "M": M, "K": K, "N": N, "a": wl.a, "b": wl.b, "buffer_sets": nsets, "graph": args.graph,
             "factors": args.factors, "clip": not args.no_clip,

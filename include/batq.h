@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BATQ_ABI_VERSION 3
+#define BATQ_ABI_VERSION 4
 
 typedef enum {
   BATQ_OK = 0,
@@ -260,9 +260,7 @@ int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * X_bf16: [M][ldx] bf16, 1 <= M <= 32 (M == 0 or N == 0 is a no-op), K a
  * multiple of 256, ldx >= K and a multiple of 8, X 16-byte aligned.  A, B,
  * r_hi, r_lo: as for batq_act_transform_quant (ratios may both be NULL: no
- * clipping).  factors: NULL, or the block transforms prepared from the same
- * A and B by batq_decode_prepare_factors (16-byte aligned; faster, same
- * results).  Wp: packed weights for (N, K), 16-byte aligned.  Y: [M][N] bf16
+ * clipping).  Wp: packed weights for (N, K), 16-byte aligned.  Y: [M][N] bf16
  * or float, 4-byte aligned.  Xq [M][K/2] (8-byte aligned) and Xs [M][K/32]:
  * optional, both NULL or both set; when set they also receive the quantised
  * activations.  workspace: device memory of at least
@@ -274,25 +272,10 @@ int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * Errors: SHAPE (also a workspace that is too small), NULL, ALIGN,
  * UNSUPPORTED (factor size or output type), HIP. */
 batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                             const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                             const float* A, const float* B, const float* r_hi,
                              const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
                              uint8_t* Xq, uint8_t* Xs, void* workspace, int64_t workspace_bytes,
                              hipStream_t stream);
-
-/* Bytes of the prepared block transforms of a K-channel layer for the decode
- * step: K/32 x 6144.  -1 for K not a positive multiple of 256.  Host only. */
-int64_t batq_decode_factors_bytes(int64_t K);
-
-/* Offline, once per layer (like the weights): the decode step's block
- * transforms P_i = B_i (x) A prepared as the exact three-way bf16 split of
- * P_i^T in the matrix-core operand order, the same bits the decode kernel
- * would build from A and B_i [en.papernotes.org, Key Designs §2: one shared
- * A, a private B_i per block].  Passed as `factors` to the decode calls, it
- * replaces the per-call rebuild of every P_i (results identical bit for bit).
- * A: [a][a], B: [K/32][b][b] float (device); factors: batq_decode_factors_bytes(K)
- * bytes, 16-byte aligned.  Errors: SHAPE, UNSUPPORTED, NULL, ALIGN, HIP. */
-batq_status batq_decode_prepare_factors(int64_t K, int32_t a, int32_t b, const float* A, const float* B,
-                                        uint8_t* factors, hipStream_t stream);
 
 /* ------------------------------------------------ fused decode, no allocation
  * For callers that cannot allocate device memory or pass a workspace: code
@@ -319,7 +302,7 @@ int64_t batq_decode_noalloc_scratch_bytes(void);
  * Errors: as batq_w4a4_decode; TOO_LARGE (see above); HIP (also the address
  * lookup failing). */
 batq_status batq_w4a4_decode_noalloc(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                                     const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                                     const float* A, const float* B, const float* r_hi,
                                      const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
                                      uint8_t* Xq, uint8_t* Xs, hipStream_t stream);
 

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.batq_abi_version() == 3
+    assert lib.batq_abi_version() == 4
     for s in range(8):
         assert lib.batq_status_str(s) and lib.batq_status_str(s) != b"unknown status"
     assert lib.batq_status_str(99) == b"unknown status"
@@ -171,9 +171,9 @@ def test_decode_workspace_bytes(lib):
     assert f(4, 256, 100) == -1 and f(4, 256, 0) == -1 and f(4, -1, 256) == -1
 
 
-def _dec(lib, x=FAKE, M=4, K=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, fa=0, rh=0, rl=0, wp=FAKE, N=256, y=FAKE, out=0,
+def _dec(lib, x=FAKE, M=4, K=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0, wp=FAKE, N=256, y=FAKE, out=0,
          xq=0, xs=0, ws=FAKE, wsb=1 << 30):
-    return lib.batq_w4a4_decode(x, M, K, ld, a, b, A, B, fa, rh, rl, wp, N, y, out, xq, xs, ws, wsb, None)
+    return lib.batq_w4a4_decode(x, M, K, ld, a, b, A, B, rh, rl, wp, N, y, out, xq, xs, ws, wsb, None)
 
 
 def test_decode_argument_checks(lib):
@@ -196,7 +196,6 @@ def test_decode_argument_checks(lib):
     assert _dec(lib, y=FAKE + 2) == ALIGN
     assert _dec(lib, ws=FAKE + 16) == ALIGN
     assert _dec(lib, xq=FAKE + 4, xs=FAKE) == ALIGN
-    assert _dec(lib, fa=FAKE + 8) == ALIGN
     # empty batch or no columns: no-ops that return before touching the GPU
     assert _dec(lib, M=0) == OK
     assert _dec(lib, N=0) == OK
@@ -283,15 +282,3 @@ def test_probe_argument_checks(lib):
     assert lib.batq_probe_hbm_stream(FAKE, g, FAKE, 3, None) == UNSUP
     assert lib.batq_probe_hbm_stream(FAKE, g - 16, FAKE, 4, None) == SHAPE
     assert lib.batq_probe_hbm_stream(FAKE, g, 0, 4, None) == NULL
-
-
-def test_decode_prepared_factor_checks(lib):
-    assert lib.batq_decode_factors_bytes(4096) == 128 * 6144
-    assert lib.batq_decode_factors_bytes(4000) == -1 and lib.batq_decode_factors_bytes(0) == -1
-    f = lib.batq_decode_prepare_factors
-    assert f(4000, 8, 4, FAKE, FAKE, FAKE, None) == SHAPE
-    assert f(4096, 8, 8, FAKE, FAKE, FAKE, None) == SHAPE
-    assert f(4096, 3, 32 // 3, FAKE, FAKE, FAKE, None) in (SHAPE, UNSUP)
-    assert f(4096, 8, 4, 0, FAKE, FAKE, None) == NULL
-    assert f(4096, 8, 4, FAKE, FAKE, 0, None) == NULL
-    assert f(4096, 8, 4, FAKE, FAKE, FAKE + 4, None) == ALIGN

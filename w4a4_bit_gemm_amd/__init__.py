@@ -27,8 +27,6 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     w4a4_decode,
     w4a4_decode_noalloc,
-    decode_factors_bytes,
-    decode_prepare_factors,
     decode_noalloc_scratch_bytes,
     kv_cache_quant,
     probe_mfma_fp4,

@@ -76,8 +76,8 @@ def _load():
     lib.batq_decode_noalloc_scratch_bytes.restype = I64
     lib.batq_decode_noalloc_scratch_bytes.argtypes = []
     lib.batq_w4a4_decode_noalloc.restype = ctypes.c_int
-    lib.batq_w4a4_decode_noalloc.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, P, I64, P, ctypes.c_int, P,
-                                             P, P]
+    lib.batq_w4a4_decode_noalloc.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, P, ctypes.c_int, P, P,
+                                             P]
     lib.batq_probe_mfma_fp4.restype = ctypes.c_int
     lib.batq_probe_mfma_fp4.argtypes = [I64, I32, I32, ctypes.c_uint32, P, P, P]
     lib.batq_probe_stream_granule.restype = I64
@@ -89,12 +89,8 @@ def _load():
     lib.batq_probe_hbm_copy.restype = ctypes.c_int
     lib.batq_probe_hbm_copy.argtypes = [P, P, I64, P]
     lib.batq_w4a4_decode.restype = ctypes.c_int
-    lib.batq_w4a4_decode.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, P, I64, P, ctypes.c_int, P, P, P,
+    lib.batq_w4a4_decode.argtypes = [P, I64, I64, I64, I32, I32, P, P, P, P, P, I64, P, ctypes.c_int, P, P, P,
                                      I64, P]
-    lib.batq_decode_factors_bytes.restype = I64
-    lib.batq_decode_factors_bytes.argtypes = [I64]
-    lib.batq_decode_prepare_factors.restype = ctypes.c_int
-    lib.batq_decode_prepare_factors.argtypes = [I64, I32, I32, P, P, P, P]
     _lib = lib
     return lib
 
@@ -427,38 +423,8 @@ def decode_workspace(M: int, N: int, K: int, device):
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def decode_factors_bytes(K: int) -> int:
-    """Bytes of the prepared block transforms for the decode step (-1: bad K)."""
-    return int(_load().batq_decode_factors_bytes(K))
-
-
-def decode_prepare_factors(A, B, K: int, out=None):
-    """Offline, once per layer: the decode step's block transforms P_i =
-    B_i (x) A as the exact bf16 split the kernel would build (pass the result
-    as ``factors`` to :func:`w4a4_decode`; same results, less work per call)."""
-    torch = _torch()
-    a, b = _factors(A, B, K)
-    nbytes = decode_factors_bytes(K)
-    if nbytes < 0:
-        raise ValueError("prepared factors need K to be a positive multiple of 256")
-    if out is None:
-        out = torch.empty((nbytes,), dtype=torch.uint8, device=A.device)
-    else:
-        _req_shape(out, torch.uint8, (nbytes,), "out")
-    _dev(A, B, out)
-    _check(_load().batq_decode_prepare_factors(K, a, b, _ptr(A), _ptr(B), _ptr(out), _stream_ptr(torch, A.device)))
-    return out
-
-
-def _factors_arg(factors, K):
-    torch = _torch()
-    if factors is not None:
-        _req_shape(factors, torch.uint8, (decode_factors_bytes(K),), "factors")
-    return factors
-
-
 def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None, out=None,
-                quantized_out: Optional[tuple] = None, factors=None):
+                quantized_out: Optional[tuple] = None):
     """Fused decode step: transform + clip + MXFP4 quantisation of X (M <= 32
     tokens) inside the GEMM against packed weights, one launch.
 
@@ -483,10 +449,8 @@ def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None
         _req_shape(Xq, torch.uint8, (M, K // 2), "Xq (quantized_out)")
         _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (quantized_out)")
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
-    factors = _factors_arg(factors, K)
-    _dev(X, A, B, r_hi, r_lo, Wp.data, workspace, out, Xq, Xs, factors)
-    st = _load().batq_w4a4_decode(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(factors),
-                                  _ptr(r_hi), _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
+    _dev(X, A, B, r_hi, r_lo, Wp.data, workspace, out, Xq, Xs)
+    st = _load().batq_w4a4_decode(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
                                   _ptr(workspace), workspace.numel(), _stream_ptr(torch, X.device))
     _check(st)
     return out
@@ -497,8 +461,7 @@ def decode_noalloc_scratch_bytes() -> int:
     return int(_load().batq_decode_noalloc_scratch_bytes())
 
 
-def w4a4_decode_noalloc(X, A, B, r_hi, r_lo, Wp: PackedWeight, out, quantized_out: Optional[tuple] = None,
-                        factors=None):
+def w4a4_decode_noalloc(X, A, B, r_hi, r_lo, Wp: PackedWeight, out, quantized_out: Optional[tuple] = None):
     """:func:`w4a4_decode` for callers that cannot allocate: the same result,
     with the partial tiles in the library's own device array instead of a
     workspace.  ``out`` ([M, N] bf16 or float32) is required, so that nothing
@@ -519,11 +482,9 @@ def w4a4_decode_noalloc(X, A, B, r_hi, r_lo, Wp: PackedWeight, out, quantized_ou
     if quantized_out is not None:
         _req_shape(Xq, torch.uint8, (M, K // 2), "Xq (quantized_out)")
         _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (quantized_out)")
-    factors = _factors_arg(factors, K)
-    _dev(X, A, B, r_hi, r_lo, Wp.data, out, Xq, Xs, factors)
+    _dev(X, A, B, r_hi, r_lo, Wp.data, out, Xq, Xs)
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
-    st = _load().batq_w4a4_decode_noalloc(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(factors),
-                                          _ptr(r_hi),
+    st = _load().batq_w4a4_decode_noalloc(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi),
                                           _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
                                           _stream_ptr(torch, X.device))
     _check(st)

@@ -264,7 +264,7 @@ namespace {
 
 // Checks shared by both decode entry points (everything but the workspace).
 batq_status check_decode_args(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                              const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                              const float* A, const float* B, const float* r_hi,
                               const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
                               uint8_t* Xq, uint8_t* Xs) {
   if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || N > batq::kDecodeMaxN || K <= 0 || K % 256 != 0 || ldx < K)
@@ -274,7 +274,7 @@ batq_status check_decode_args(const void* X_bf16, int64_t M, int64_t K, int64_t 
   if (out != BATQ_OUT_BF16 && out != BATQ_OUT_F32) return BATQ_ERR_UNSUPPORTED;
   if (X_bf16 == nullptr || A == nullptr || B == nullptr || Wp == nullptr || Y == nullptr) return BATQ_ERR_NULL;
   if ((r_hi == nullptr) != (r_lo == nullptr) || (Xq == nullptr) != (Xs == nullptr)) return BATQ_ERR_NULL;
-  if (!aligned(X_bf16, 16) || ldx % 8 != 0 || !aligned(Wp, 16) || !aligned(Y, 4) || !aligned(factors, 16))
+  if (!aligned(X_bf16, 16) || ldx % 8 != 0 || !aligned(Wp, 16) || !aligned(Y, 4))
     return BATQ_ERR_ALIGN;
   if (!aligned(A, 4) || !aligned(B, 4) || (r_hi && (!aligned(r_hi, 4) || !aligned(r_lo, 4))) ||
       (Xq && !aligned(Xq, 8)))
@@ -283,7 +283,7 @@ batq_status check_decode_args(const void* X_bf16, int64_t M, int64_t K, int64_t 
 }
 
 batq_status run_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, const float* A,
-                       const float* B, const uint8_t* factors, const float* r_hi, const float* r_lo,
+                       const float* B, const float* r_hi, const float* r_lo,
                        const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out, uint8_t* Xq, uint8_t* Xs,
                        void* part, hipStream_t stream) {
   batq::DecodeArgs args;
@@ -303,55 +303,39 @@ batq_status run_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, in
   args.xq = Xq;
   args.xs = Xs;
   args.part = static_cast<float*>(part);
-  args.pprep = factors;
   return batq::launch_decode_fused(args, stream) == hipSuccess ? BATQ_OK : BATQ_ERR_HIP;
 }
 
 }  // namespace
 
 batq_status batq_w4a4_decode(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                             const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                             const float* A, const float* B, const float* r_hi,
                              const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
                              uint8_t* Xq, uint8_t* Xs, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   const batq_status st =
-      check_decode_args(X_bf16, M, K, ldx, a, b, A, B, factors, r_hi, r_lo, Wp, N, Y, out, Xq, Xs);
+      check_decode_args(X_bf16, M, K, ldx, a, b, A, B, r_hi, r_lo, Wp, N, Y, out, Xq, Xs);
   if (st != BATQ_OK) return st;
   if (workspace == nullptr) return BATQ_ERR_NULL;
   if (!aligned(workspace, 256)) return BATQ_ERR_ALIGN;
   if (workspace_bytes < batq::decode_workspace_bytes(M, N, K)) return BATQ_ERR_SHAPE;
   if (M == 0 || N == 0) return BATQ_OK;
-  return run_decode(X_bf16, M, K, ldx, a, A, B, factors, r_hi, r_lo, Wp, N, Y, out, Xq, Xs, workspace, stream);
+  return run_decode(X_bf16, M, K, ldx, a, A, B, r_hi, r_lo, Wp, N, Y, out, Xq, Xs, workspace, stream);
 }
 
 int64_t batq_decode_noalloc_scratch_bytes(void) { return batq::kDecodeScratchBytes; }
 
 batq_status batq_w4a4_decode_noalloc(const void* X_bf16, int64_t M, int64_t K, int64_t ldx, int32_t a, int32_t b,
-                                     const float* A, const float* B, const uint8_t* factors, const float* r_hi,
+                                     const float* A, const float* B, const float* r_hi,
                                      const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
                                      uint8_t* Xq, uint8_t* Xs, hipStream_t stream) {
   const batq_status st =
-      check_decode_args(X_bf16, M, K, ldx, a, b, A, B, factors, r_hi, r_lo, Wp, N, Y, out, Xq, Xs);
+      check_decode_args(X_bf16, M, K, ldx, a, b, A, B, r_hi, r_lo, Wp, N, Y, out, Xq, Xs);
   if (st != BATQ_OK) return st;
   if (batq::decode_workspace_bytes(M, N, K) > batq::kDecodeScratchBytes) return BATQ_ERR_TOO_LARGE;
   if (M == 0 || N == 0) return BATQ_OK;
   void* part = nullptr;
   if (batq::decode_scratch(&part) != hipSuccess || part == nullptr) return BATQ_ERR_HIP;
-  return run_decode(X_bf16, M, K, ldx, a, A, B, factors, r_hi, r_lo, Wp, N, Y, out, Xq, Xs, part, stream);
-}
-
-int64_t batq_decode_factors_bytes(int64_t K) {
-  if (K <= 0 || K % 256 != 0) return -1;
-  return batq::decode_factors_bytes(K);
-}
-
-batq_status batq_decode_prepare_factors(int64_t K, int32_t a, int32_t b, const float* A, const float* B,
-                                        uint8_t* factors, hipStream_t stream) {
-  if (K <= 0 || K % 256 != 0 || (int64_t)a * (int64_t)b != 32) return BATQ_ERR_SHAPE;
-  if (!is_pow2_factor(a)) return BATQ_ERR_UNSUPPORTED;
-  if (A == nullptr || B == nullptr || factors == nullptr) return BATQ_ERR_NULL;
-  if (!aligned(A, 4) || !aligned(B, 4) || !aligned(factors, 16)) return BATQ_ERR_ALIGN;
-  return batq::launch_decode_prepare_factors(A, B, K, log2_exact(a), factors, stream) == hipSuccess ? BATQ_OK
-                                                                                                     : BATQ_ERR_HIP;
+  return run_decode(X_bf16, M, K, ldx, a, A, B, r_hi, r_lo, Wp, N, Y, out, Xq, Xs, part, stream);
 }
 
 batq_status batq_kv_cache_quant(const void* KV_bf16, int64_t T, int64_t HD, int64_t ld, int32_t a, int32_t b,

@@ -97,17 +97,9 @@ struct DecodeArgs {
   uint8_t* xq;          // optional [M][K/2] codes and [M][K/32] scales, or nullptr
   uint8_t* xs;
   float* part;          // workspace: arrival counters, then fp32 partial tiles [N/128][splits][M][128]
-  const uint8_t* pprep = nullptr;  // optional prepared P_i splits (decode_factors_bytes), else from A, B
 };
 int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_decode_fused(const DecodeArgs& args, hipStream_t stream);
-// Prepared block transforms for the decode step: per 32-channel block, the
-// exact three-way bf16 split of P_i^T in MFMA operand order (6 x 64 lanes x
-// 16 bytes), the same bits the kernels compute from A and B_i.
-constexpr int64_t kDecodeFactorBlockBytes = 6 * 64 * 16;
-inline int64_t decode_factors_bytes(int64_t K) { return (K / 32) * kDecodeFactorBlockBytes; }
-hipError_t launch_decode_prepare_factors(const float* A, const float* B, int64_t K, int a_log2, uint8_t* out,
-                                         hipStream_t stream);
 // Arrival counters of the decode step's K splits: the first bytes of every
 // workspace, one 32-bit counter per 128-column chunk (N up to 524288).
 constexpr int64_t kDecodeCounterBytes = 16384;

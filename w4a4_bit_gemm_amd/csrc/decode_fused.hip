@@ -114,30 +114,6 @@ __device__ __forceinline__ ActIn load_act(const DecodeArgs& p, int64_t blk, int 
   in.rl = p.r_lo ? p.r_lo[blk] : 1.0f;
   return in;
 }
-// The tokens' channels and the ratios only (prepared transforms).
-__device__ __forceinline__ ActIn load_x_ratios(const DecodeArgs& p, int64_t blk, int j, int h) {
-  ActIn in;
-  const int64_t row = j < p.M ? j : p.M - 1;
-  const uint16_t* xr = p.x + row * p.ldx + blk * 32 + 8 * h;
-  in.x0 = *reinterpret_cast<const uint4*>(xr);
-  in.x1 = *reinterpret_cast<const uint4*>(xr + 16);
-  in.rh = p.r_hi ? p.r_hi[blk] : 1.0f;
-  in.rl = p.r_lo ? p.r_lo[blk] : 1.0f;
-  return in;
-}
-// Prepared split of block blk: parts hi[0], hi[1], mid[0], mid[1], lo[0],
-// lo[1], each 64 lanes x 16 bytes.
-__device__ __forceinline__ PSplit load_prepared(const uint8_t* __restrict__ pp, int64_t blk, int lane) {
-  const uint8_t* b = pp + blk * kDecodeFactorBlockBytes + 16 * lane;
-  PSplit ps;
-  ps.hi[0] = ld16(b);
-  ps.hi[1] = ld16(b + 1024);
-  ps.mid[0] = ld16(b + 2048);
-  ps.mid[1] = ld16(b + 3072);
-  ps.lo[0] = ld16(b + 4096);
-  ps.lo[1] = ld16(b + 5120);
-  return ps;
-}
 __device__ __forceinline__ uint4 zero_unless(bool keep, uint4 v) {
   return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
@@ -151,10 +127,7 @@ __device__ __forceinline__ int tile_row(int r, int g) { return 8 * (r >> 2) + 4 
 // calls left them at zero (never under an earlier call's partials).
 __host__ __device__ constexpr int64_t counter_bytes(int64_t) { return kDecodeCounterBytes; }
 
-// PREP: the split of each P_i comes prepared (6 coalesced loads per block)
-// instead of being built from the factors (10 loads and ~140 vector
-// instructions per block, repeated by every workgroup of a K split).
-template <int LA, bool PREP>
+template <int LA>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_fused_kernel(DecodeArgs p, int nchunk, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[kSplitStages][32 * kQRow];
   __shared__ __attribute__((aligned(16))) uint8_t ss[kSplitStages][32 * 8];
@@ -174,16 +147,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_fused_kernel(DecodeArgs
 
   // 1. activation side of block `wave` of every stage, then the weights.
   ActIn in[kSplitStages];
-  PSplit pre[kSplitStages];
 #pragma unroll
   for (int t = 0; t < kSplitStages; ++t) {  // a stage past the split's end reloads its last one (unused)
     const int64_t blk = (s0 + (t < nstage ? t : nstage - 1)) * 8 + wave;
-    if constexpr (PREP) {
-      in[t] = load_x_ratios(p, blk, j, h);
-      pre[t] = load_prepared(p.pprep, blk, lane);
-    } else {
-      in[t] = load_act<LA>(p, blk, j, h);
-    }
+    in[t] = load_act<LA>(p, blk, j, h);
   }
   __builtin_amdgcn_sched_barrier(0);
   const int gsel = wave % kGroups;  // 32-column group within the chunk
@@ -207,7 +174,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_fused_kernel(DecodeArgs
   for (int t = 0; t < kSplitStages; ++t) {
     if (t >= nstage) break;
     const int64_t blk = (s0 + t) * 8 + wave;
-    const PSplit ps = PREP ? pre[t] : split_p(in[t].f);
+    const PSplit ps = split_p(in[t].f);
     const f32x16 acc = transform_block(ps, zero_unless(j < p.M, in[t].x0), zero_unless(j < p.M, in[t].x1));
     int sbyte;
     const uint2 code = quant_block_e2m1(acc, in[t].rh, in[t].rl, h, sbyte);
@@ -326,31 +293,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_fused_kernel(DecodeArgs
 
 template <int LA>
 hipError_t launch_t(const DecodeArgs& a, int nchunk, int nsplit, hipStream_t stream) {
-  if (a.pprep != nullptr)
-    hipLaunchKernelGGL((decode_fused_kernel<LA, true>), dim3(nchunk * nsplit), dim3(64 * kDecWaves), 0, stream, a,
-                       nchunk, nsplit);
-  else
-    hipLaunchKernelGGL((decode_fused_kernel<LA, false>), dim3(nchunk * nsplit), dim3(64 * kDecWaves), 0, stream, a,
-                       nchunk, nsplit);
+  hipLaunchKernelGGL((decode_fused_kernel<LA>), dim3(nchunk * nsplit), dim3(64 * kDecWaves), 0, stream, a, nchunk,
+                     nsplit);
   return hipGetLastError();
-}
-
-// One wave per block: the split the decode kernel would build, stored in
-// the prepared layout.
-__global__ __launch_bounds__(256) void decode_prepare_factors_kernel(const float* A, const float* B, int64_t nb,
-                                                                     int la, uint8_t* out) {
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nb) return;
-  const int lane = threadIdx.x & 63;
-  const int bdim = 32 >> la;
-  const PSplit ps = split_p(load_p_factors(A, B + blk * bdim * bdim, la, lane & 31, lane >> 5));
-  uint4* o = reinterpret_cast<uint4*>(out + blk * kDecodeFactorBlockBytes) + lane;
-  o[0] = ps.hi[0];
-  o[64] = ps.hi[1];
-  o[128] = ps.mid[0];
-  o[192] = ps.mid[1];
-  o[256] = ps.lo[0];
-  o[320] = ps.lo[1];
 }
 
 }  // namespace
@@ -359,14 +304,6 @@ int64_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t nchunk = (N + kChunkCols - 1) / kChunkCols, nst = K / 256;
   const int64_t nsplit = (nst + kSplitStages - 1) / kSplitStages;
   return nsplit > 1 ? counter_bytes(nchunk) + nchunk * nsplit * M * kChunkCols * 4 : 0;
-}
-
-hipError_t launch_decode_prepare_factors(const float* A, const float* B, int64_t K, int a_log2, uint8_t* out,
-                                         hipStream_t stream) {
-  const int64_t nb = K / 32;
-  hipLaunchKernelGGL(decode_prepare_factors_kernel, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, A, B, nb,
-                     a_log2, out);
-  return hipGetLastError();
 }
 
 hipError_t decode_scratch(void** ptr) {
