@@ -428,7 +428,7 @@ def measure_ceilings(torch, w, dev, act_read_bytes=None, act_write_ratio=4):
     nbytes = (2 << 30) // gran * gran  # 2 GiB
     assert nbytes == 2 << 30, gran
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-    rsink = torch.empty(2048, dtype=torch.int32, device=dev)
+    rsink = torch.empty(4096, dtype=torch.int32, device=dev)
     csrc = src[: nbytes // 8]
     cdst = torch.empty(nbytes // 8, dtype=torch.int32, device=dev)
 

@@ -34,13 +34,13 @@ batq_status batq_probe_mfma_fp4(int64_t workgroups, int32_t iters, int32_t rando
                                 unsigned long long* clocks, hipStream_t stream);
 
 /* Stream sizes must be positive multiples of this many bytes (256 threads x 8
- * loads x 16 bytes); a stream runs on up to 2048 workgroups, each reading a
- * contiguous range. */
+ * loads x 16 bytes); a stream runs on up to 4096 workgroups, each reading a
+ * contiguous range with non-temporal 16-byte loads. */
 int64_t batq_probe_stream_granule(void);
 
 /* Reads `bytes` of src (16-byte aligned) once with 16-byte loads, each
  * workgroup streaming a contiguous range; sink receives one xor word per
- * workgroup (room for 2048 uint32).  Errors: SHAPE (bytes not a multiple of the
+ * workgroup (room for 4096 uint32).  Errors: SHAPE (bytes not a multiple of the
  * granule), NULL, ALIGN, HIP. */
 batq_status batq_probe_hbm_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 

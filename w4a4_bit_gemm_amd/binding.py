@@ -535,10 +535,10 @@ def probe_stream_granule() -> int:
 
 
 def probe_hbm_read(src, sink):
-    """Streaming read of all of src (any dtype, contiguous); sink int32 [2048]."""
+    """Streaming read of all of src (any dtype, contiguous); sink int32 [4096]."""
     torch = _torch()
     _req(src, src.dtype, "src")
-    _req_shape(sink, torch.int32, (2048,), "sink")
+    _req_shape(sink, torch.int32, (4096,), "sink")
     _dev(src, sink)
     _check(_load().batq_probe_hbm_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                        _stream_ptr(torch, src.device)))
