@@ -240,13 +240,16 @@ batq_status batq_kv_cache_quant(const void* KV_bf16, int64_t T, int64_t HD, int6
  * the pages report the online transform's cost as the decode overhead].
  */
 #define BATQ_DECODE_MAX_M 32
+/* Largest K of the decode calls: 8191 K splits of two 256-k stages (the
+ * kernel counts splits in 13 bits). */
+#define BATQ_DECODE_MAX_K 4193792
 
 /* Workspace bytes batq_w4a4_decode needs for (M, N, K): 16 KiB of arrival
  * counters, then fp32 partial tiles, one per 128-column chunk, K split and
  * token, where a K split covers two 256-k stages; 0 when K is at most 512 (one
  * split: Y is written directly, no workspace is touched).
  * -1 for M outside [0, 32], N outside [0, 524288] or K not a positive
- * multiple of 256. */
+ * multiple of 256 up to 4193792 (8191 K splits). */
 int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Y[M][N] = deq(Q(X P)) deq(Wp)^T with the activation path fused into the
@@ -258,7 +261,8 @@ int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * partials in split order and writes Y, so results are deterministic and
  * within the fp32 accumulation bound of the unsplit product.
  * X_bf16: [M][ldx] bf16, 1 <= M <= 32 (M == 0 or N == 0 is a no-op), K a
- * multiple of 256, ldx >= K and a multiple of 8, X 16-byte aligned.  A, B,
+ * multiple of 256 up to 4193792, N up to 524288, ldx >= K and a multiple of 8,
+ * X 16-byte aligned.  A, B,
  * r_hi, r_lo: as for batq_act_transform_quant (ratios may both be NULL: no
  * clipping).  Wp: packed weights for (N, K), 16-byte aligned.  Y: [M][N] bf16
  * or float, 4-byte aligned.  Xq [M][K/2] (8-byte aligned) and Xs [M][K/32]:

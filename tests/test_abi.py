@@ -176,7 +176,18 @@ def _dec(lib, x=FAKE, M=4, K=256, ld=256, a=8, b=4, A=FAKE, B=FAKE, rh=0, rl=0, 
     return lib.batq_w4a4_decode(x, M, K, ld, a, b, A, B, rh, rl, wp, N, y, out, xq, xs, ws, wsb, None)
 
 
+def test_decode_limits_match_the_header():
+    import re
+    from w4a4_bit_gemm_amd import binding as bd
+    h = open(os.path.join(ROOT, "include", "batq.h")).read()
+    assert int(re.search(r"#define BATQ_DECODE_MAX_M (\d+)", h).group(1)) == bd.DECODE_MAX_M
+    assert int(re.search(r"#define BATQ_DECODE_MAX_K (\d+)", h).group(1)) == bd.DECODE_MAX_K == 8191 * 512
+
+
 def test_decode_argument_checks(lib):
+    assert _dec(lib, K=8191 * 512 + 256, ld=8191 * 512 + 256) == SHAPE  # more K splits than the kernel counts
+    assert lib.batq_decode_workspace_bytes(4, 256, 8191 * 512 + 256) == -1
+    assert lib.batq_decode_workspace_bytes(4, 256, 8191 * 512) > 0
     assert _dec(lib, M=33) == SHAPE
     assert _dec(lib, M=-1) == SHAPE
     assert _dec(lib, K=224, ld=256) == SHAPE

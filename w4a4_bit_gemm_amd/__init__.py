@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     weight_packed_bytes,
     prepare_weight,
     weight_prep,
+    DECODE_MAX_K,
     DECODE_MAX_M,
     decode_workspace,
     decode_workspace_bytes,

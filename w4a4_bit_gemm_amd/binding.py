@@ -404,7 +404,8 @@ def packed_gemm_kernel(M: int, N: int, K: int, act_fp8: bool = False) -> int:
     return int(_load().batq_packed_gemm_kernel(M, N, K, 1 if act_fp8 else 0))
 
 
-DECODE_MAX_M = 32
+DECODE_MAX_M = 32  # BATQ_DECODE_MAX_M
+DECODE_MAX_K = 4193792  # BATQ_DECODE_MAX_K
 
 
 def decode_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -30,6 +30,12 @@ COMPILE_FLAGS = [
     "-Wno-unused-command-line-argument",
     # the GEMM kernels fully unroll their stage loops for common K (exact wait counts)
     "-mllvm", "-pragma-unroll-threshold=1000000",
+    # leading scalar kernel arguments arrive in SGPRs at wave launch, so a
+    # latency-bound kernel (the fused decode step) issues its first loads
+    # without waiting for a scalar load of its arguments; aggregate arguments
+    # are unaffected, and firmware without preloading runs the loading prologue
+    # the compiler emits
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
 ]
 LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC"]
 

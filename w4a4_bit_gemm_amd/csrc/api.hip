@@ -256,7 +256,9 @@ int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8
 }
 
 int64_t batq_decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || N > batq::kDecodeMaxN || K <= 0 || K % 256 != 0) return -1;
+  if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || N > batq::kDecodeMaxN || K <= 0 || K % 256 != 0 ||
+      K > BATQ_DECODE_MAX_K)
+    return -1;
   return batq::decode_workspace_bytes(M, N, K);
 }
 
@@ -267,7 +269,8 @@ batq_status check_decode_args(const void* X_bf16, int64_t M, int64_t K, int64_t 
                               const float* A, const float* B, const float* r_hi,
                               const float* r_lo, const uint8_t* Wp, int64_t N, void* Y, batq_out_dtype out,
                               uint8_t* Xq, uint8_t* Xs) {
-  if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || N > batq::kDecodeMaxN || K <= 0 || K % 256 != 0 || ldx < K)
+  if (M < 0 || M > BATQ_DECODE_MAX_M || N < 0 || N > batq::kDecodeMaxN || K <= 0 || K % 256 != 0 ||
+      K > BATQ_DECODE_MAX_K || ldx < K)
     return BATQ_ERR_SHAPE;
   if ((int64_t)a * (int64_t)b != 32) return BATQ_ERR_SHAPE;
   if (!is_pow2_factor(a)) return BATQ_ERR_UNSUPPORTED;
