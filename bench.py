@@ -592,6 +592,13 @@ def main():
     t_act = loop_seconds(act)
     t_gemm = loop_seconds(gemm)
 
+    # The two kernels' own times must fit inside the step they make up (5 %
+    # for box noise).  Below 30 us per step a loop of one kernel alone runs at
+    # the host's launch rate, so there the check does not apply.
+    consistent = bool((t_act + t_gemm) <= 1.05 * t_step or t_step < 30e-6)
+    if not consistent:
+        print(f"bench: per-kernel times {1e6 * t_act:.2f} + {1e6 * t_gemm:.2f} us exceed the step's "
+              f"{1e6 * t_step:.2f} us", file=sys.stderr)
     flops = 2.0 * M * N * K
     act_bytes = M * K * 2 + M * xq_row + M * K // 32  # algorithmic: read bf16, write codes + scales
     gemm_bytes = M * xq_row + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2
@@ -661,6 +668,7 @@ def main():
         },
         "step": {"gpu_us": t_step * 1e6, "kernels_sum_us": (t_act + t_gemm) * 1e6,
                  "kernels_sum_over_step": (t_act + t_gemm) / t_step,
+                 "consistent": consistent,
                  "timing": "step: events around the timed steps; kernels: events around a loop of each kernel alone"},
         "cpu_baseline": None,
     }
