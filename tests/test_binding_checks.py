@@ -49,6 +49,11 @@ def test_act_transform_quant_rejections():
     refused(f, g["X"], g["A"], g["B"], out=(u8(M, K // 2).float(), u8(M, K // 32)), match="uint8")
     # the MXFP8 variant wants one byte per element
     refused(bd.act_transform_quant_mxfp8, g["X"], g["A"], g["B"], out=(u8(M, K // 2), u8(M, K // 32)), match="Xq")
+    # activations may be a column slice of a wider matrix (row stride > K), but
+    # not a transposed or column-strided view
+    refused(f, bf16(K, M).t(), g["A"], g["B"], match="unit column stride")
+    refused(f, bf16(M, 2 * K)[:, ::2], g["A"], g["B"], match="unit column stride")
+    refused(f, bf16(M, K + 64)[:, :K], g["A"], g["B"], match="CUDA")  # accepted up to the device check
     # right shapes, wrong device
     refused(f, g["X"], g["A"], g["B"], g["r_hi"], g["r_lo"], match="CUDA")
     refused(f, g["X"], g["A"], g["B"], out=(u8(M, K // 2), u8(M, K // 32)), match="CUDA")

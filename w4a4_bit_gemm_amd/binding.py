@@ -213,6 +213,29 @@ def _rows2d(X, dtype, name):
         raise ValueError(f"{name} must be 2-D, got {tuple(X.shape)}")
 
 
+def _rows2d_strided(X, dtype, name):
+    """A 2-D row-major matrix whose rows may be further apart than their
+    length (a column slice of a wider matrix): unit column stride, row stride
+    at least the row length; the C ABI takes the row stride as ``ld`` and
+    checks its alignment."""
+    torch = _torch()
+    if not isinstance(X, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if X.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {X.dtype}")
+    if X.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {tuple(X.shape)}")
+    if X.shape[0] > 1 and (X.stride(1) != 1 or X.stride(0) < X.shape[1]):
+        raise ValueError(f"{name} must have unit column stride and a row stride of at least its row length")
+    if X.shape[0] <= 1 and not X.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ld(X) -> int:
+    """Row stride in elements (a single row's stride is its length)."""
+    return X.stride(0) if X.shape[0] > 1 else X.shape[1]
+
+
 def act_transform_quant(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple] = None):
     """Fused block transform + clip + MXFP4 quantisation of bf16 activations.
 
@@ -230,7 +253,7 @@ def act_transform_quant_mxfp8(X, A, B, r_hi=None, r_lo=None, out: Optional[tuple
 
 def _act(X, A, B, r_hi, r_lo, out, fp8: bool):
     torch = _torch()
-    _rows2d(X, torch.bfloat16, "X")
+    _rows2d_strided(X, torch.bfloat16, "X")
     M, K = X.shape
     a, b = _factors(A, B, K)
     _ratios(r_hi, r_lo, (K // 32,))
@@ -244,7 +267,7 @@ def _act(X, A, B, r_hi, r_lo, out, fp8: bool):
         _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (out)")
     _dev(X, A, B, r_hi, r_lo, Xq, Xs)
     fn = _load().batq_act_transform_quant_mxfp8 if fp8 else _load().batq_act_transform_quant
-    st = fn(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Xq), _ptr(Xs),
+    st = fn(_ptr(X), M, K, _ld(X), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Xq), _ptr(Xs),
             _stream_ptr(torch, X.device))
     _check(st)
     return Xq, Xs
@@ -257,7 +280,7 @@ def weight_prep(W, AinvT, BinvT, wr_hi=None, wr_lo=None, out: Optional[tuple] = 
     ratios or None.  Returns (Wq uint8 [N, K/2], Ws uint8 [N, K/32]).
     """
     torch = _torch()
-    _rows2d(W, torch.bfloat16, "W")
+    _rows2d_strided(W, torch.bfloat16, "W")
     N, K = W.shape
     a, b = _factors(AinvT, BinvT, K, names=("AinvT", "BinvT"))
     _ratios(wr_hi, wr_lo, (N, K // 32), names=("wr_hi", "wr_lo"))
@@ -269,7 +292,7 @@ def weight_prep(W, AinvT, BinvT, wr_hi=None, wr_lo=None, out: Optional[tuple] = 
         _req_shape(Wq, torch.uint8, (N, K // 2), "Wq (out)")
         _req_shape(Ws, torch.uint8, (N, K // 32), "Ws (out)")
     _dev(W, AinvT, BinvT, wr_hi, wr_lo, Wq, Ws)
-    st = _load().batq_weight_prep(_ptr(W), N, K, W.stride(0), a, b, _ptr(AinvT),
+    st = _load().batq_weight_prep(_ptr(W), N, K, _ld(W), a, b, _ptr(AinvT),
                                   _ptr(BinvT), _ptr(wr_hi), _ptr(wr_lo), _ptr(Wq), _ptr(Ws),
                                   _stream_ptr(torch, W.device))
     _check(st)
@@ -435,7 +458,7 @@ def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None
     receive the quantised activations.  Returns Y [M, N].
     """
     torch = _torch()
-    _rows2d(X, torch.bfloat16, "X")
+    _rows2d_strided(X, torch.bfloat16, "X")
     M, K = X.shape
     a, b = _factors(A, B, K)
     _ratios(r_hi, r_lo, (K // 32,))
@@ -451,7 +474,7 @@ def w4a4_decode(X, A, B, r_hi, r_lo, Wp: PackedWeight, workspace, out_dtype=None
         _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (quantized_out)")
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
     _dev(X, A, B, r_hi, r_lo, Wp.data, workspace, out, Xq, Xs)
-    st = _load().batq_w4a4_decode(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
+    st = _load().batq_w4a4_decode(_ptr(X), M, K, _ld(X), a, b, _ptr(A), _ptr(B), _ptr(r_hi), _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
                                   _ptr(workspace), workspace.numel(), _stream_ptr(torch, X.device))
     _check(st)
     return out
@@ -468,7 +491,7 @@ def w4a4_decode_noalloc(X, A, B, r_hi, r_lo, Wp: PackedWeight, out, quantized_ou
     workspace.  ``out`` ([M, N] bf16 or float32) is required, so that nothing
     is allocated on this path either.  Calls that overlap on one GPU race."""
     torch = _torch()
-    _rows2d(X, torch.bfloat16, "X")
+    _rows2d_strided(X, torch.bfloat16, "X")
     M, K = X.shape
     a, b = _factors(A, B, K)
     _ratios(r_hi, r_lo, (K // 32,))
@@ -485,7 +508,7 @@ def w4a4_decode_noalloc(X, A, B, r_hi, r_lo, Wp: PackedWeight, out, quantized_ou
         _req_shape(Xs, torch.uint8, (M, K // 32), "Xs (quantized_out)")
     _dev(X, A, B, r_hi, r_lo, Wp.data, out, Xq, Xs)
     code = BATQ_OUT_F32 if out_dtype == torch.float32 else BATQ_OUT_BF16
-    st = _load().batq_w4a4_decode_noalloc(_ptr(X), M, K, X.stride(0), a, b, _ptr(A), _ptr(B), _ptr(r_hi),
+    st = _load().batq_w4a4_decode_noalloc(_ptr(X), M, K, _ld(X), a, b, _ptr(A), _ptr(B), _ptr(r_hi),
                                           _ptr(r_lo), _ptr(Wp.data), N, _ptr(out), code, _ptr(Xq), _ptr(Xs),
                                           _stream_ptr(torch, X.device))
     _check(st)
@@ -498,7 +521,7 @@ def kv_cache_quant(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s, fmt: int = 4):
     MXFP4) or [rows, H*D] (fmt 8, MXFP8 E4M3) uint8, cache_s [rows, H*D/32]
     uint8.  Rows of the cache not named by a slot are left untouched."""
     torch = _torch()
-    _rows2d(KV, torch.bfloat16, "KV")
+    _rows2d_strided(KV, torch.bfloat16, "KV")
     T, HD = KV.shape
     a, b = _factors(A, B, HD)
     _ratios(r_hi, r_lo, (HD // 32,))
@@ -510,7 +533,7 @@ def kv_cache_quant(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s, fmt: int = 4):
     _req_shape(cache_q, torch.uint8, (rows, HD if fmt == 8 else HD // 2), "cache_q")
     _req_shape(cache_s, torch.uint8, (rows, HD // 32), "cache_s")
     _dev(KV, A, B, r_hi, r_lo, slots, cache_q, cache_s)
-    st = _load().batq_kv_cache_quant(_ptr(KV), T, HD, KV.stride(0), a, b, _ptr(A), _ptr(B),
+    st = _load().batq_kv_cache_quant(_ptr(KV), T, HD, _ld(KV), a, b, _ptr(A), _ptr(B),
                                      _ptr(r_hi), _ptr(r_lo), _ptr(slots), rows, fmt, _ptr(cache_q), _ptr(cache_s),
                                      _stream_ptr(torch, KV.device))
     _check(st)
