@@ -80,8 +80,9 @@ hipError_t launch_mxfp4_gemm_packed(const GemmArgs& args, hipStream_t stream);
 bool packed_dma_applies(const GemmArgs& args);
 hipError_t launch_mxfp4_gemm_packed_dma(const GemmArgs& args, hipStream_t stream);
 // Fused decode step (decode_fused.hip): transform + clip + MXFP4 quantisation
-// of M <= 32 tokens inside the GEMM on packed weights, split over
-// (256-column chunk, K split), then a split-order reduction launch.
+// of M <= 32 tokens inside the GEMM on packed weights, one launch split over
+// (128-column chunk, K split of two 256-k stages); the last workgroup of each
+// chunk adds its splits' partial tiles in split order.
 struct DecodeArgs {
   const uint16_t* x;    // [M][ldx] bf16
   int64_t ldx;
