@@ -24,8 +24,10 @@
  *     saturating to 6, sign kept (a negative value rounding to 0 is code 0x8).
  *   - Device pointers unless the name ends in _host.  Every device call is
  *     asynchronous on `stream` (0 = the null stream).  The library never
- *     allocates, frees or synchronises, keeps no pointer after returning and
- *     holds no mutable global state: calls on distinct streams are thread-safe.
+ *     allocates, frees or synchronises and keeps no pointer after returning.
+ *     Its only mutable global state is the device array of the no-allocation
+ *     decode entry point (calls of that entry point that overlap on one GPU
+ *     race); every other call on distinct streams is thread-safe.
  *   - The caller owns every buffer and keeps it alive until the stream work
  *     completes.
  *   - Errors: every argument check runs on the host before any HIP call and
