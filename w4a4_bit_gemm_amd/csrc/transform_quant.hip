@@ -115,8 +115,16 @@ struct TQSmem {
 // byte per element (the W4A8 setting); otherwise MXFP4 (E2M1), two per byte.
 // STREAM: non-temporal code and scale stores, for outputs that the next
 // kernel does not read (cache rows written through the slot mapping).
+// Tile walk.  Default (t1 == 0): workgroup x gy + y takes column group x and
+// tile rows y, y + gy, ...  Skewed (t1 > 0; the grid is exactly two
+// workgroups per CU): workgroups are dispatched in id order, one per CU
+// first, and the first one on a CU runs ahead of the second (measured: it
+// ends ~6 us earlier on 16-tile workgroups).  So the first half of the ids
+// takes t1 consecutive tile rows each and the second half t2 = 2 t - t1,
+// with gy / 2 workgroups per column in each half; ids that share a tile row
+// stay congruent mod 8 (same XCD) as in the default walk.
 template <bool PER_ROW, bool F8, bool STREAM>
-__device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& p, int64_t gy) {
+__device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& p, int64_t gy, int t1) {
   using T = TQSmem<F8>;
   constexpr int kXPolicy = (F8 && STREAM) ? 0 : kStreamLoad;
   constexpr int kRing = T::kRing;
@@ -131,11 +139,25 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
   // Workgroup id = x gy + y: with gy a multiple of 8, every column group x of
   // tile row y lands on the same XCD (ids go to the XCDs in turn), so the
   // 8-byte scale pieces of a row's 128-byte scale line merge in one L2.
-  const int64_t blk0 = ((int64_t)blockIdx.x / gy) * kBlocksPerWG;
   const int64_t tiles = (p.rows + kTT - 1) / kTT;
-  const int64_t ty0 = (int64_t)blockIdx.x % gy;
-  const int64_t tstep = gy;
-  const int64_t ntile = ty0 < tiles ? (tiles - ty0 + tstep - 1) / tstep : 0;  // uniform per workgroup
+  int64_t blk0, ty0, tstep, ntile;  // uniform per workgroup
+  if (t1 == 0) {
+    blk0 = ((int64_t)blockIdx.x / gy) * kBlocksPerWG;
+    ty0 = (int64_t)blockIdx.x % gy;
+    tstep = gy;
+    ntile = ty0 < tiles ? (tiles - ty0 + tstep - 1) / tstep : 0;
+  } else {
+    const int64_t pairs = gy / 2;                    // workgroups per column in each half
+    const int64_t half = (int64_t)gridDim.x / 2;
+    const int64_t set = (int64_t)blockIdx.x / half;  // 0: dispatched first
+    const int64_t r = (int64_t)blockIdx.x % half;
+    const int64_t k = r % pairs;
+    const int64_t t2 = 2 * (tiles / gy) - t1;
+    blk0 = (r / pairs) * kBlocksPerWG;
+    ty0 = set == 0 ? k * t1 : pairs * t1 + k * t2;
+    tstep = 1;
+    ntile = set == 0 ? t1 : t2;
+  }
   const int64_t nblk = (nb - blk0) < kBlocksPerWG ? (nb - blk0) : kBlocksPerWG;  // valid blocks here
 
   // ---------------------------------------------------------- compute waves
@@ -303,15 +325,15 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
 
 template <bool PER_ROW, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
-    TransformQuantArgs p, int64_t gy) {
-  transform_quant_tiles<PER_ROW, F8, false>(p, gy);
+    TransformQuantArgs p, int64_t gy, int t1) {
+  transform_quant_tiles<PER_ROW, F8, false>(p, gy, t1);
 }
 
 // Cache rows are not read by the next kernel, so they are streamed past L2.
 template <bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kv_cache_quant_kernel(
-    TransformQuantArgs p, int64_t gy) {
-  transform_quant_tiles<false, F8, true>(p, gy);
+    TransformQuantArgs p, int64_t gy, int t1) {
+  transform_quant_tiles<false, F8, true>(p, gy, t1);
 }
 
 }  // namespace
@@ -337,22 +359,27 @@ hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t st
   if (gy > cap) gy = cap;
   if (gy > tiles) gy = tiles;
   const dim3 grid((unsigned)(gx * gy));
+  // Skewed walk (see transform_quant_tiles) where the grid is two workgroups
+  // per CU of 16 or more equal walks: 17 tiles against 15 at 16 per
+  // workgroup, 4.8 % less time on 16384 x 4096 (alternating A/B).
+  int t1 = 0;
+  if (gx * gy == 512 && gy % 16 == 0 && tiles % gy == 0 && tiles / gy >= 16) t1 = (int)(tiles / gy + tiles / gy / 16);
   const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
   if (args.slot != nullptr && !per_row) {
     if (args.fp8)
-      hipLaunchKernelGGL((kv_cache_quant_kernel<true>), grid, dim3(kThreads), 0, stream, args, gy);
+      hipLaunchKernelGGL((kv_cache_quant_kernel<true>), grid, dim3(kThreads), 0, stream, args, gy, t1);
     else
-      hipLaunchKernelGGL((kv_cache_quant_kernel<false>), grid, dim3(kThreads), 0, stream, args, gy);
+      hipLaunchKernelGGL((kv_cache_quant_kernel<false>), grid, dim3(kThreads), 0, stream, args, gy, t1);
   } else if (args.fp8) {
     if (per_row)
-      hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args, gy);
+      hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args, gy, t1);
     else
-      hipLaunchKernelGGL((transform_quant_kernel<false, true>), grid, dim3(kThreads), 0, stream, args, gy);
+      hipLaunchKernelGGL((transform_quant_kernel<false, true>), grid, dim3(kThreads), 0, stream, args, gy, t1);
   } else {
     if (per_row)
-      hipLaunchKernelGGL((transform_quant_kernel<true, false>), grid, dim3(kThreads), 0, stream, args, gy);
+      hipLaunchKernelGGL((transform_quant_kernel<true, false>), grid, dim3(kThreads), 0, stream, args, gy, t1);
     else
-      hipLaunchKernelGGL((transform_quant_kernel<false, false>), grid, dim3(kThreads), 0, stream, args, gy);
+      hipLaunchKernelGGL((transform_quant_kernel<false, false>), grid, dim3(kThreads), 0, stream, args, gy, t1);
   }
   return hipGetLastError();
 }
