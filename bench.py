@@ -477,7 +477,7 @@ def run_ceilings(args, torch, w, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
     fp8 = args.act_format == "mxfp8"

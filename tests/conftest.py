@@ -32,9 +32,9 @@ def pytest_terminal_summary(terminalreporter):
         tr.write_line(f"{r['label'][:44]:44s} {r['elements']:11d} {r['mismatches']:5d} "
                       f"{r['mismatches_outside_literal']:8d} {r['literal_exempt']:8d} {r['free']:6d} "
                       f"{r['free_blocks']:8d} {r['mismatches'] / r['elements']:9.1e}")
-    out = os.path.join(ROOT, "gpurun_out")
-    if os.path.isdir(out):
+    out = os.environ.get("BATQ_PARITY_JSON")  # optional: also keep the counts as JSON at this path
+    if out:
         import json
 
-        with open(os.path.join(out, "parity_counts.json"), "w") as f:
+        with open(out, "w") as f:
             json.dump(parity.RESULTS, f, indent=1)
