@@ -211,6 +211,26 @@ def test_act_full_config(w, cfg):
     note(f"  {st}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_act_skewed_walk_equals_row_slices(w, fp8):
+    """At 16384 x 4096 the transform runs two workgroups per CU with 16 tiles
+    each, which takes the skewed tile walk (the first-dispatched half of the
+    workgroups takes 17 consecutive tile rows, the second half 15).  Rows are
+    independent, so the whole must equal the same rows transformed as 2048-row
+    slices, which take the strided walk."""
+    note(f"case: act skewed walk vs row slices fp8={fp8}")
+    wl = gen.make_workload(5, with_weights=False)
+    X = dev_bf16(wl.X_bits)
+    A, B = dev_f32(wl.A), dev_f32(wl.B)
+    rh, rl = dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta))
+    fn = w.act_transform_quant_mxfp8 if fp8 else w.act_transform_quant
+    q, s = fn(X, A, B, rh, rl)
+    for r0 in range(0, wl.M, 2048):
+        qs, ss = fn(X[r0:r0 + 2048], A, B, rh, rl)
+        assert torch.equal(qs, q[r0:r0 + 2048]) and torch.equal(ss, s[r0:r0 + 2048]), r0
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("a", gen.SWEEP_A)
 def test_act_shared_factor_sweep(w, a):
     note(f"case: act sweep a={a} (config 5 shape)")

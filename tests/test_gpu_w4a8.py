@@ -125,7 +125,7 @@ def test_act8_zero_tiny_and_single_sign_blocks(w):
     assert same.all(), np.argwhere(~same)[:5].tolist()
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_act8_full_config(w, cfg):
     note(f"case: act mxfp8 full config {cfg}")
     wl = gen.make_workload(cfg, with_weights=False)
