@@ -81,11 +81,6 @@ __device__ __forceinline__ PSplit split_p(const PFactors& f) {
   }
   return ps;
 }
-__device__ __forceinline__ PSplit build_p_split(const float* __restrict__ A, const float* __restrict__ Bi, int la,
-                                                int j, int h) {
-  return split_p(load_p_factors(A, Bi, la, j, h));
-}
-
 // y for one block and 32 tokens: x0 / x1 are the lane's 8 bf16 channels
 // 8 h .. 8 h + 7 and 16 + 8 h .. 16 + 8 h + 7 of token j; the parts are
 // accumulated lo -> mid -> hi in fp32.

@@ -123,6 +123,37 @@ struct TQSmem {
 // takes t1 consecutive tile rows each and the second half t2 = 2 t - t1,
 // with gy / 2 workgroups per column in each half; ids that share a tile row
 // stay congruent mod 8 (same XCD) as in the default walk.
+// The lane's factor entries, as load_p_factors gives them, with fewer loads
+// when a >= 8: each run of 8 consecutive k = 16 ks + 8 h + t then lies in one
+// row of B_i and in 8 consecutive rows of A, and for a <= 16 the lane's two
+// runs read the same rows of A.  At a = 8 that is 10 loads instead of 32.
+// These are the workgroup's first loads after the loader's tile requests, so
+// fewer of them wait less behind that traffic.
+__device__ __forceinline__ PFactors load_factor_runs(const float* __restrict__ A, const float* __restrict__ Bi, int la,
+                                                     int j, int h) {
+  if (la < 3) return load_p_factors(A, Bi, la, j, h);
+  const int a = 1 << la, amask = a - 1, bdim = 32 >> la;
+  PFactors f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const float bv = Bi[((16 * ks + 8 * h) >> la) * bdim + (j >> la)];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.bv[ks][t] = bv;
+  }
+  const int r0 = (8 * h) & amask, ja = j & amask;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f.av[0][t] = A[(r0 + t) * a + ja];
+  if (la <= 4) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.av[1][t] = f.av[0][t];
+  } else {
+    const int r1 = (16 + 8 * h) & amask;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.av[1][t] = A[(r1 + t) * a + ja];
+  }
+  return f;
+}
+
 template <bool PER_ROW, bool F8, bool STREAM>
 __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& p, int64_t gy, int t1) {
   using T = TQSmem<F8>;
@@ -213,7 +244,8 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
   }
 
   // P_i^T as MFMA A operand, exact three-way bf16 split.
-  const PSplit ps = build_p_split(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h);
+  const PSplit ps =
+      split_p(load_factor_runs(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h));
   // Ratios shared by every token (activations) are read once here.
   const bool clip = p.r_hi != nullptr;
   const bool per_row = PER_ROW && clip;
