@@ -67,6 +67,9 @@ def parse():
                     help="with --decode: replay the steps from a captured HIP graph (no host launch overhead)")
     ap.add_argument("--kv-cache", type=int, choices=[4, 8], default=None,
                     help="KV-cache write of the config's tokens, 8 heads x 128 channels, MXFP4 (4) or MXFP8 (8)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only the GEMM: the packed W4A4 GEMM beside hipBLASLt's MXFP4 GEMM on the same operands "
+                         "(large prefill only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (HBM counter calibration)")
@@ -474,6 +477,108 @@ def run_ceilings(args, torch, w, dev):
                                                      "hbm_GBs": HBM_PEAK_GBS}}), flush=True)
 
 
+def run_vendor_gemm(args, torch, w, wl, dev):
+    """The packed W4A4 GEMM beside hipBLASLt's block-scaled MXFP4 GEMM
+    (include/batq_vendor.h) on the same operands: this workload's activations
+    through the transform kernel and its prepared weights, quantised once.
+    Both GEMMs run `steps` launches over the same rotating buffer sets (more
+    bytes than the Infinity Cache), with events at the loop's two ends.  Every
+    algorithm hipBLASLt's heuristic offers (up to 8) is timed, and each one's output is
+    compared with the packed GEMM's: how many bf16 outputs differ from its fp32
+    result rounded to nearest even (its own bf16 output) and rounded toward
+    zero, and the largest difference from the fp32 result relative to max |Y|.
+    The packed GEMM is timed before and after the library's loops; the faster
+    loop counts.  Large prefill only: at 2048 x 12288 x 4096 the library's first
+    calls did not return within three minutes."""
+    from w4a4_bit_gemm_amd import vendor_gemm as vg
+
+    M, K, N = wl.M, wl.K, wl.N
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    rh, rl = f32(w.clip_ratios(wl.alpha)), f32(w.clip_ratios(wl.beta))
+    Xq0, Xs0 = w.act_transform_quant(bf16(wl.X_bits), f32(wl.A), f32(wl.B), rh, rl)
+    Wq0, Ws0 = w.prepare_weight(bf16(wl.W_bits), wl.A, wl.B, wl.walpha, wl.wbeta)
+    torch.cuda.synchronize()
+    set_bytes = M * K // 2 + M * K // 32 + 2 * (N * K // 2 + N * K // 32) + M * N * 2
+    nsets = min(64, max(2, int(np.ceil(2.2 * CACHE_BYTES / set_bytes))))
+    sets = [dict(Xq=Xq0.clone(), Xs=Xs0.clone(), Wq=Wq0.clone(), Ws=Ws0.clone(), Wp=w.weight_pack(Wq0, Ws0),
+                 Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    plan = vg.VendorGemm(M, N, K, dev, max_algos=8)
+    torch.cuda.synchronize()
+    print(f"vendor: hipBLASLt offers {plan.algos} algorithms", file=sys.stderr, flush=True)
+
+    def loop_us(fn):
+        for i in range(min(args.warmup, 10)):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    def ours(i):
+        s = sets[i % nsets]
+        w.mxfp4_gemm_packed(s["Xq"], s["Xs"], s["Wp"], out=s["Y"])
+
+    ours(0)
+    y32 = w.mxfp4_gemm_packed(sets[0]["Xq"], sets[0]["Xs"], sets[0]["Wp"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref = sets[0]["Y"].clone()  # bf16: the fp32 result rounded to nearest even
+    ref_max = float(y32.abs().max())
+    # the fp32 result rounded toward zero to bf16 (low 16 bits dropped)
+    y_rz = (y32.view(torch.int32) >> 16).to(torch.int16)
+    t_ours_first = loop_us(ours)
+    print(f"vendor: packed GEMM {t_ours_first:.1f} us", file=sys.stderr, flush=True)
+    per_algo = []
+    y_v = torch.empty_like(y_ref)
+    for a in range(plan.algos):
+        s0 = sets[0]
+        try:
+            plan.run(a, s0["Xq"], s0["Xs"], s0["Wq"], s0["Ws"], y_v)
+        except RuntimeError as e:  # an algorithm the library offers but then refuses to run
+            per_algo.append({"algo": a, "error": str(e)})
+            continue
+        torch.cuda.synchronize()
+        differ = int((y_v.view(torch.int16) != y_ref.view(torch.int16)).sum())
+        differ_rz = int((y_v.view(torch.int16) != y_rz).sum())
+        max_rel = float((y_v.float() - y32).abs().max()) / ref_max
+
+        def theirs(i, a=a):
+            s = sets[i % nsets]
+            plan.run(a, s["Xq"], s["Xs"], s["Wq"], s["Ws"], s["Y"])
+
+        per_algo.append({"algo": a, "us": loop_us(theirs), "outputs": M * N, "differ_from_batq_bf16": differ,
+                         "differ_from_batq_fp32_rounded_to_zero": differ_rz,
+                         "max_diff_to_batq_fp32_over_max_abs": max_rel})
+        # each algorithm's first launch takes seconds inside the library
+        print(f"vendor: algorithm {a}: {per_algo[-1]['us']:.1f} us", file=sys.stderr, flush=True)
+    plan.close()
+    t_ours_after = loop_us(ours)  # again, after the library's loops, on a GPU as warm as theirs
+    print(f"vendor: packed GEMM {t_ours_after:.1f} us", file=sys.stderr, flush=True)
+    t_ours = min(t_ours_first, t_ours_after)
+    flops = 2.0 * M * N * K
+    best = min((r for r in per_algo if "us" in r), key=lambda r: r["us"])
+    kernel = ("mxfp4_gemm_packed_dma_kernel" if w.packed_gemm_kernel(M, N, K) == 1 else "mxfp4_gemm_packed_kernel")
+    print(json.dumps({
+        "comparison": "packed W4A4 GEMM against hipBLASLt's MXFP4 GEMM (VEC32_UE8M0 scales), same operands, bf16 out",
+        "config": {"workload": f"{wl.name}: {M}x{K} activations (transform kernel, a={wl.a}) x {N}x{K} prepared "
+                               f"weights", "M": M, "N": N, "K": K, "buffer_sets": nsets, "steps": args.steps},
+        "batq": {"kernel": kernel, "us": t_ours, "us_before_after": [t_ours_first, t_ours_after],
+                 "TFLOP/s": flops / t_ours / 1e6, "frac_mfma": flops / t_ours / 1e6 / MXFP4_PEAK_TFLOPS},
+        "hipblaslt": {"version": vg.version(), "algos": len(per_algo), "best": best,
+                      "TFLOP/s": flops / best["us"] / 1e6, "per_algo": per_algo},
+        "batq_speedup_over_best": best["us"] / t_ours,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -505,6 +610,12 @@ def main():
         return
     if args.kv_cache:
         run_kv(args, torch, w, wl, dev)
+        return
+    if args.vendor_gemm:
+        if args.config != 5:
+            print("--vendor-gemm runs on the large prefill (--config 5) only", file=sys.stderr)
+            sys.exit(2)
+        run_vendor_gemm(args, torch, w, wl, dev)
         return
 
     def bf16(bits):

@@ -293,3 +293,42 @@ def test_probe_argument_checks(lib):
     assert lib.batq_probe_hbm_stream(FAKE, g, FAKE, 3, None) == UNSUP
     assert lib.batq_probe_hbm_stream(FAKE, g - 16, FAKE, 4, None) == SHAPE
     assert lib.batq_probe_hbm_stream(FAKE, g, 0, 4, None) == NULL
+
+
+VENDOR_HEADER = os.path.join(ROOT, "include", "batq_vendor.h")
+
+
+@pytest.fixture(scope="module")
+def vendor_lib():
+    from w4a4_bit_gemm_amd import vendor_gemm
+
+    return vendor_gemm._load()
+
+
+def test_vendor_library_exports_every_declared_symbol(vendor_lib):
+    names = declared_functions((VENDOR_HEADER,))
+    assert {"batq_vendor_gemm_create", "batq_vendor_gemm_run", "batq_vendor_gemm_algos",
+            "batq_vendor_gemm_destroy", "batq_vendor_version", "batq_vendor_last_status"} <= set(names)
+    for name in names:
+        assert hasattr(vendor_lib, name), name
+
+
+def test_vendor_library_is_separate_from_the_path(lib):
+    # the comparison GEMM is not in libbatq.so, and libbatq.so does not link hipBLASLt
+    assert not hasattr(lib, "batq_vendor_gemm_create")
+    from w4a4_bit_gemm_amd import binding
+
+    with open(binding.library_path(), "rb") as f:
+        assert b"libhipblaslt" not in f.read()
+
+
+def test_vendor_argument_checks_before_any_library_call(vendor_lib):
+    plan = ctypes.c_void_p(FAKE)
+    for M, N, K, algos in ((0, 16, 64, 4), (16, -1, 64, 4), (16, 16, 48, 4), (16, 16, 64, 0), (16, 16, 64, 65)):
+        assert vendor_lib.batq_vendor_gemm_create(M, N, K, algos, 0, ctypes.byref(plan)) == -1
+        assert plan.value is None  # cleared on failure
+        plan = ctypes.c_void_p(FAKE)
+    assert vendor_lib.batq_vendor_gemm_create(16, 16, 64, 4, 0, None) == -1
+    assert vendor_lib.batq_vendor_gemm_algos(None) == -1
+    assert vendor_lib.batq_vendor_gemm_run(None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    vendor_lib.batq_vendor_gemm_destroy(None)

@@ -1,4 +1,5 @@
-"""Build libbatq.so (all HIP sources, gfx950) in-tree with hipcc.
+"""Build libbatq.so (all HIP sources, gfx950) in-tree with hipcc, and
+libbatq_vendor.so (the hipBLASLt comparison GEMM of include/batq_vendor.h).
 
 Each source compiles to its own object in parallel (the GEMM files fully
 unroll their stage loops and dominate the time), then one link makes the
@@ -17,6 +18,10 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libbatq.so")
+# hipBLASLt's MXFP4 GEMM behind include/batq_vendor.h: a comparison for the
+# benchmark, linked on its own so that libbatq.so does not depend on hipBLASLt
+VENDOR_LIB = os.path.join(PKG, "libbatq_vendor.so")
+VENDOR_SRC = os.path.join(PKG, "vendor", "hipblaslt_mxfp4.cpp")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 COMPILE_FLAGS = [
@@ -79,7 +84,21 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_filter(res.stderr)}")
     os.replace(tmp, LIB)
+    build_vendor(verbose)
     return LIB
+
+
+def build_vendor(verbose: bool = False) -> str:
+    tmp = VENDOR_LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared", "-I", os.path.join(ROOT, "include"),
+           VENDOR_SRC, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lhipblaslt", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {os.path.basename(VENDOR_SRC)} ({res.returncode}):\n{_filter(res.stderr)}")
+    os.replace(tmp, VENDOR_LIB)
+    return VENDOR_LIB
 
 
 if __name__ == "__main__":
