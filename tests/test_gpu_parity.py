@@ -454,14 +454,17 @@ def run_gemm_packed(w, xc, xs, wc, ws, dtype):
     return Y.float().cpu().numpy().astype(np.float64)
 
 
-# K / 256 in {1, 2, 4, 8, 16, 48} take the fully unrolled kernels; 3, 6, 12 the
-# looped one.  M and N cover partial row and column tiles.  The last five
+# K / 256 in {1, 2, 4, 8, 16, 48} take the fully unrolled kernels; 3, 6, 12, 13,
+# 20, 25 the looped one, whose body covers 12 stages (13, 20 and 25 end inside
+# a second or third pass, 20 with four-stage scale groups, 13 and 25 without).
+# M and N cover partial row and column tiles.  The last five
 # shapes have more than 256 tiles of 128 x 256 with K / 256 in {4, 8, 48}: they
 # run the two-workgroups-per-CU kernel (direct-to-LDS activation loads); N =
 # 33001 gives output rows that are not whole 16-byte chunks (scalar stores).
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (33, 47, 256), (128, 256, 512), (130, 250, 768),
                                    (257, 129, 1024), (40, 33, 1536), (200, 300, 2048), (64, 520, 3072),
-                                   (64, 300, 4096), (129, 257, 12288), (2000, 12200, 1024),
+                                   (64, 300, 4096), (129, 257, 12288), (96, 200, 3328), (130, 300, 5120),
+                                   (64, 96, 6400), (2000, 12200, 1024),
                                    (4000, 8000, 1024), (2100, 8300, 2048), (2100, 4200, 12288),
                                    (1000, 33001, 1024)])
 def test_packed_gemm_matches_oracle_and_unpacked(w, M, N, K):

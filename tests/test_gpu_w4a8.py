@@ -158,10 +158,11 @@ def run_gemm8(w, xc, xs, wc, ws, out_dtype):
     return y.float().cpu().numpy().astype(np.float64)
 
 
-# K / 256 in {1, 2, 4, 8, 16, 48}: unrolled kernels; 3, 6, 12: the looped one.
+# K / 256 in {1, 2, 4, 8, 16, 48}: unrolled kernels; 3, 6, 12, 13, 20: the looped
+# one, whose body covers 4 stages (20 with four-stage scale groups, 13 without).
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (33, 47, 256), (128, 256, 512), (130, 250, 768),
                                    (257, 129, 1024), (40, 33, 1536), (200, 300, 2048), (64, 520, 3072),
-                                   (64, 300, 4096), (129, 257, 12288)])
+                                   (64, 300, 4096), (129, 257, 12288), (40, 70, 3328), (66, 90, 5120)])
 def test_w4a8_gemm_matches_oracle(w, M, N, K):
     """Random E4M3 activations (all finite codes, subnormals included) and E2M1
     weights, block scales over 2^-17 .. 2^7: every product is exact, so the
