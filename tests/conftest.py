@@ -26,10 +26,10 @@ def pytest_terminal_summary(terminalreporter):
         return
     tr = terminalreporter
     tr.section("parity counts (codes/scales vs oracle)")
-    tr.write_line(f"{'comparison':44s} {'elements':>11s} {'mism':>5s} {'out-1e-6':>8s} {'1e-6 set':>8s} "
-                  f"{'free':>6s} {'free blk':>8s} {'mism/elem':>9s}")
+    tr.write_line(f"{'comparison':44s} {'elements':>11s} {'mism':>5s} {'+0/-0':>5s} {'out-1e-6':>8s} "
+                  f"{'1e-6 set':>8s} {'free':>6s} {'free blk':>8s} {'mism/elem':>9s}")
     for r in parity.RESULTS:
-        tr.write_line(f"{r['label'][:44]:44s} {r['elements']:11d} {r['mismatches']:5d} "
+        tr.write_line(f"{r['label'][:44]:44s} {r['elements']:11d} {r['mismatches']:5d} {r['signed_zero']:5d} "
                       f"{r['mismatches_outside_literal']:8d} {r['literal_exempt']:8d} {r['free']:6d} "
                       f"{r['free_blocks']:8d} {r['mismatches'] / r['elements']:9.1e}")
     out = os.environ.get("BATQ_PARITY_JSON")  # optional: also keep the counts as JSON at this path

@@ -669,3 +669,62 @@ def test_kv_cache_rows_places_valid_slots_only():
     src = ob.kv_cache_rows(np.array([5, 0, -1, 9, 3, 10]), 10)
     assert src.tolist() == [1, -1, -1, 4, -1, 0, -1, -1, -1, 3]
     assert (ob.kv_cache_rows(np.array([], dtype=np.int64), 4) == -1).all()
+
+
+def test_large_operand_rows_match_a_per_group_rotation():
+    """gen.large_rows (the host side of the >2 GiB parity tests) equals the
+    device-side construction those tests use, here run with torch on the CPU:
+    each group of base-size rows rotated by whole blocks, distinct per group."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    R0, K = 64, 128
+    base = rng.integers(0, 16, size=(R0, K), dtype=np.uint8)
+    rows = 5 * R0 + 17
+    src = torch.from_numpy(base)
+    full = torch.empty((rows, K), dtype=src.dtype)
+    for g in range((rows + R0 - 1) // R0):
+        n = min(R0, rows - g * R0)
+        full[g * R0:g * R0 + n] = torch.roll(src[:n], gen.large_group_shift(g, 32, K // 32), dims=1)
+    pick = np.array([0, 1, R0 - 1, R0, 2 * R0 + 5, rows - 1])
+    assert np.array_equal(full.numpy()[pick], gen.large_rows(base, pick, 32, K // 32))
+    # the packed-byte form rotates by 16 bytes per 32 codes
+    packed = torch.from_numpy(ob.pack_codes(base))
+    g = 3
+    assert np.array_equal(torch.roll(packed, gen.large_group_shift(g, 16, K // 32), dims=1).numpy(),
+                          ob.pack_codes(gen.large_rows(base, np.arange(g * R0, (g + 1) * R0), 32, K // 32)))
+    # rows of different groups differ; the rotation repeats after K / 32 groups
+    assert not np.array_equal(full.numpy()[5], full.numpy()[R0 + 5])
+    assert gen.large_group_shift(K // 32, 32, K // 32) == 0
+
+
+def test_compare_quant_signed_zero_and_the_stated_window():
+    """The parity rule on a synthetic block (scale 2^0, no clip): a +0 / -0
+    mismatch passes where the fp32 error can flip the value's sign, and fails
+    where it cannot; a free mismatch 3e-6 relative from a boundary still fails
+    the stated 1e-6 window."""
+    from tests import parity
+
+    y = np.ones((1, 32))
+    S = np.ones((1, 32))
+    y[0, 0], S[0, 0] = 6.0, 6.0                   # block max: shared exponent 0
+    y[0, 1], S[0, 1] = -2.3e-9, 0.5               # |y| far below gamma_36 S: sign free
+    y[0, 2], S[0, 2] = -0.1, 0.1                  # rounds to -0, sign fixed
+    y[0, 3], S[0, 3] = 0.75 * (1 + 3e-6), 5.0     # free, 3e-6 above the 0.75 boundary
+    dec = ob.decisions(y, S, None, None)
+    assert dec.scales[0, 0] == 127
+    assert dec.codes[0, 1:4].tolist() == [8, 8, 2]
+    assert dec.elem_free[0, 1] and not dec.elem_free[0, 2] and dec.elem_free[0, 3]
+    assert not dec.zero_sign_free[0, 1]
+
+    def run(k, code):
+        c = dec.codes.copy()
+        c[0, k] = code
+        return parity.compare_quant(ob.pack_codes(c), dec.scales.copy(), dec, label="synthetic", max_frac=1.0)
+
+    st = run(1, 0)
+    assert (st["mismatches"], st["signed_zero"], st["mismatches_outside_literal"]) == (1, 1, 0)
+    with pytest.raises(AssertionError, match="outside the free set"):
+        run(2, 0)
+    with pytest.raises(AssertionError, match="outside the stated 1e-6 window"):
+        run(3, 1)
+    parity.RESULTS[:] = [r for r in parity.RESULTS if r["label"] != "synthetic"]  # not a run's comparison

@@ -198,3 +198,27 @@ def make_custom(M: int, K: int, N: int, a: int = 8, seed: int = 0, x_kind: str =
     wbeta = rng.normal(3.0, 0.5, (N, nb)).astype(np.float32)
     return Workload(f"custom_{M}x{K}x{N}_a{a}_s{seed}", 0, M, K, N, a, b, f64_to_bf16_bits(x),
                     f64_to_bf16_bits(W), A, B, alpha, beta, walpha, wbeta, meta={"x_kind": x_kind})
+
+
+# ------------------------------------------------------------ large operands
+#
+# Operands larger than 2 GiB are built from a seeded base of R0 rows: row r of
+# the large operand is base row r % R0, its columns rotated by `unit` times
+# (r // R0) % `period` positions (whole MX blocks), so that every group of R0
+# rows differs from the others and a row read from the wrong group gives
+# different values.  The device side applies the same rotation per group
+# (large_group_shift); the host side rebuilds any sampled row (large_rows).
+
+
+def large_group_shift(group: int, unit: int, period: int) -> int:
+    """Column rotation of row group `group` (rows group*R0 .. group*R0 + R0 - 1)."""
+    return unit * (group % period)
+
+
+def large_rows(base: np.ndarray, rows: np.ndarray, unit: int, period: int) -> np.ndarray:
+    """Rows `rows` of the large operand built from `base` (see above)."""
+    R0 = base.shape[0]
+    out = np.empty((len(rows), base.shape[1]), dtype=base.dtype)
+    for i, r in enumerate(np.asarray(rows, dtype=np.int64)):
+        out[i] = np.roll(base[r % R0], large_group_shift(int(r // R0), unit, period))
+    return out
