@@ -15,7 +15,8 @@
 //   activation scales the same way, four stages (32 bytes of a row) per load,
 //                     two-group ring;
 //   weights           packed, lane-ordered records straight into registers,
-//                     one stage ahead (two register sets);
+//                     one stage ahead (two register sets), the loads spread
+//                     between the MFMAs of the stage before;
 //   fragments         each sub-step's four activation fragments are read just
 //                     before its eight MFMAs (the other workgroup hides them).
 // Each wave waits only for its own loads (exact vmcnt), then one workgroup
@@ -109,6 +110,23 @@ __device__ __forceinline__ int64_t opaque_stage(int64_t s) {
     n##_12 = bl16(wrs1, lane16, o_ + 2048); n##_13 = bl16(wrs1, lane16, o_ + 3072);            \
     n##_s1 = bl4(wrs1, lane4, o_ + 4096);                                                      \
   }
+// The loads a step issues for later stages go out between its MFMAs, each
+// right after one MFMA of a sub-step (the scheduling groups below pin that
+// order), rather than in front of the first MFMA.  There they held each
+// wave's in-order issue back behind the queue of vector loads at every stage
+// start.  Spread out, the results are bit-identical and the GEMM is faster on
+// the 16384 x 4096 x 4096 and 2048 x 12288 x 4096 shapes (alternating A/B in
+// one process): 4.6 and 6.6 % with E2M1 activations, 3.3 and 3.1 % with
+// E4M3.  The issue order within a step is unchanged, so its vmcnt waits are
+// too.  DMA_ILk: k (MFMA, load) pairs, then the sub-step's other MFMAs.
+#define DMA_MV(J) __builtin_amdgcn_sched_group_barrier(0x008, 1, J); __builtin_amdgcn_sched_group_barrier(0x020, 1, J);
+#define DMA_IL2(J) DMA_MV(J) DMA_MV(J) __builtin_amdgcn_sched_group_barrier(0x008, 6, J);
+#define DMA_IL3(J) DMA_MV(J) DMA_MV(J) DMA_MV(J) __builtin_amdgcn_sched_group_barrier(0x008, 5, J);
+#define DMA_IL4(J) DMA_MV(J) DMA_MV(J) DMA_MV(J) DMA_MV(J) __builtin_amdgcn_sched_group_barrier(0x008, 4, J);
+#define DMA_IL5(J) DMA_MV(J) DMA_MV(J) DMA_MV(J) DMA_MV(J) DMA_MV(J) __builtin_amdgcn_sched_group_barrier(0x008, 3, J);
+// One 16-byte (DMA_W) or 4-byte (DMA_WS) part of a weight record.
+#define DMA_W(R, WRS, ST, OFF) R = bl16(WRS, lane16, (int)(opaque_stage(ST) * kPackGroupBytes) + (OFF));
+#define DMA_WS(R, WRS, ST) R = bl4(WRS, lane4, (int)(opaque_stage(ST) * kPackGroupBytes) + 4096);
 // One descriptor per 32-column group, based at its first record (a group's
 // NST records stay under 2 GiB: checked on the host), and the lane offsets of
 // a record's code (16 l) and scale (4 l) bytes.
@@ -297,45 +315,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   // takes its sub-steps in order, so the results are unchanged.
 #define DMA_RD(SLOT, FO, I) *reinterpret_cast<const uint4*>((SLOT) + (FO) + 4096 * (I))
 #define DMA_SUB(SLOT, FO, J, n)                                                                \
-  {                                                                                            \
-    uint4 fa_[kMT];                                                                            \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) fa_[i] = DMA_RD(SLOT, FO, i);              \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i)                                            \
-      acc[i][0] = mfma_fp4<J>(fa_[i], n##_0##J, sa_[i], n##_s0, acc[i][0]);                   \
-    _Pragma("unroll") for (int i = kMT - 1; i >= 0; --i)                                       \
-      acc[i][1] = mfma_fp4<J>(fa_[i], n##_1##J, sa_[i], n##_s1, acc[i][1]);                   \
-  }
-  // One stage; the lane parts of the LDS addresses are recomputed per stage
-  // (behind an empty asm) so that they are not held for every stage at once.
-#define DMA_MMA_STAGE(SLOT, SG, SQI, n)                                                         \
-  {                                                                                            \
-    uint32_t so_ = r32 * 16 + 4 * g;                                                           \
-    uint32_t fo0_ = r32 * kRowBytes + 16 * ((4 * g) ^ swz(r32));                                \
-    uint32_t fo1_ = r32 * kRowBytes + 16 * ((4 * g + 1) ^ swz(r32));                            \
-    uint32_t fo2_ = r32 * kRowBytes + 16 * ((4 * g + 2) ^ swz(r32));                            \
-    uint32_t fo3_ = r32 * kRowBytes + 16 * ((4 * g + 3) ^ swz(r32));                            \
-    asm volatile("" : "+v"(so_), "+v"(fo0_), "+v"(fo1_), "+v"(fo2_), "+v"(fo3_));              \
-    uint32_t sa_[kMT];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 512 * ((SQI) >> 1) + 8 * ((SQI) & 1)); \
-    DMA_SUB(SLOT, fo0_, 0, n)                                                                  \
-    DMA_SUB(SLOT, fo1_, 1, n)                                                                  \
-    DMA_SUB(SLOT, fo2_, 2, n)                                                                  \
-    DMA_SUB(SLOT, fo3_, 3, n)                                                                  \
-  }
+  uint4 fa_[kMT];                                                                              \
+  _Pragma("unroll") for (int i = 0; i < kMT; ++i) fa_[i] = DMA_RD(SLOT, FO, i);                \
+  _Pragma("unroll") for (int i = 0; i < kMT; ++i)                                              \
+    acc[i][0] = mfma_fp4<J>(fa_[i], n##_0##J, sa_[i], n##_s0, acc[i][0]);                     \
+  _Pragma("unroll") for (int i = kMT - 1; i >= 0; --i)                                         \
+    acc[i][1] = mfma_fp4<J>(fa_[i], n##_1##J, sa_[i], n##_s1, acc[i][1]);
+  // The lane parts of a stage's LDS addresses are recomputed per stage (behind
+  // an empty asm) so that they are not held for every stage at once.
+#define DMA_OFFSETS(SG, SQI)                                                                   \
+  uint32_t so_ = r32 * 16 + 4 * g;                                                             \
+  uint32_t fo0_ = r32 * kRowBytes + 16 * ((4 * g) ^ swz(r32));                                  \
+  uint32_t fo1_ = r32 * kRowBytes + 16 * ((4 * g + 1) ^ swz(r32));                              \
+  uint32_t fo2_ = r32 * kRowBytes + 16 * ((4 * g + 2) ^ swz(r32));                              \
+  uint32_t fo3_ = r32 * kRowBytes + 16 * ((4 * g + 3) ^ swz(r32));                              \
+  asm volatile("" : "+v"(so_), "+v"(fo0_), "+v"(fo1_), "+v"(fo2_), "+v"(fo3_));                \
+  uint32_t sa_[kMT];                                                                           \
+  _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 512 * ((SQI) >> 1) + 8 * ((SQI) & 1));
   // Step S: wait for stage S (weights issued one step ago, codes two, scale
-  // group at least two), barrier, issue weights S + 1 then the loads of stage
-  // S + 2, compute stage S.
+  // group at least two), barrier, compute stage S while issuing the loads of
+  // stages S + 1 (weights over sub-steps 0-2) and S + 2 (scale group, codes).
 #define DMA_STEP(S, CUR, NXT2, SG, SGN, BCUR, BNXT1)                                           \
   {                                                                                            \
     wait_vm(((S) + 1 < NST) ? (kQPerWave + (((S) + 1) % 4 == 0 ? 1 : 0)) : 0);                 \
     block_barrier();                                                                           \
-    if ((S) + 1 < NST) { DMA_LOAD_B(BNXT1, (S) + 1) }                                          \
-    if ((S) + 2 < NST) {                                                                       \
-      if (((S) + 2) % 4 == 0) { DMA_S(SGN, ((S) + 2) / 4) }                                    \
-      DMA_A(NXT2, (S) + 2)                                                                     \
+    sched_fence();                                                                             \
+    DMA_OFFSETS(SG, (S) % 4)                                                                   \
+    {                                                                                          \
+      DMA_SUB(CUR, fo0_, 0, BCUR)                                                              \
+      if ((S) + 1 < NST) {                                                                     \
+        DMA_W(BNXT1##_00, wrs0, (S) + 1, 0) DMA_W(BNXT1##_01, wrs0, (S) + 1, 1024)              \
+        DMA_W(BNXT1##_02, wrs0, (S) + 1, 2048) DMA_W(BNXT1##_03, wrs0, (S) + 1, 3072)           \
+        DMA_IL4(0)                                                                             \
+      }                                                                                        \
     }                                                                                          \
     sched_fence();                                                                             \
-    DMA_MMA_STAGE(CUR, SG, (S) % 4, BCUR)                                                      \
+    {                                                                                          \
+      DMA_SUB(CUR, fo1_, 1, BCUR)                                                              \
+      if ((S) + 1 < NST) {                                                                     \
+        DMA_WS(BNXT1##_s0, wrs0, (S) + 1) DMA_W(BNXT1##_10, wrs1, (S) + 1, 0)                   \
+        DMA_W(BNXT1##_11, wrs1, (S) + 1, 1024) DMA_W(BNXT1##_12, wrs1, (S) + 1, 2048)           \
+        DMA_IL4(1)                                                                             \
+      }                                                                                        \
+    }                                                                                          \
+    sched_fence();                                                                             \
+    {                                                                                          \
+      DMA_SUB(CUR, fo2_, 2, BCUR)                                                              \
+      if ((S) + 1 < NST) {                                                                     \
+        DMA_W(BNXT1##_13, wrs1, (S) + 1, 3072) DMA_WS(BNXT1##_s1, wrs1, (S) + 1)                \
+        if ((S) + 2 < NST && ((S) + 2) % 4 == 0) {                                             \
+          DMA_S(SGN, ((S) + 2) / 4)                                                            \
+          DMA_IL3(2)                                                                           \
+        } else {                                                                               \
+          DMA_IL2(2)                                                                           \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
+    sched_fence();                                                                             \
+    {                                                                                          \
+      DMA_SUB(CUR, fo3_, 3, BCUR)                                                              \
+      if ((S) + 2 < NST) {                                                                     \
+        DMA_A(NXT2, (S) + 2)                                                                   \
+        DMA_IL4(3)                                                                             \
+      }                                                                                        \
+    }                                                                                          \
+    sched_fence();                                                                             \
   }
   // Code slots cycle with period 3 (stage s in slot s % 3), weight sets with
   // period 2, scale groups with period 8 (stage s reads group s / 4 from
@@ -370,7 +414,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     }
   }
 #undef DMA_STEP
-#undef DMA_MMA_STAGE
+#undef DMA_OFFSETS
 #undef DMA_SUB
 #undef DMA_RD
 #undef DMA_S
@@ -479,42 +523,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // not all held across the stage loop.
 #define RD8(SLOT, I, FO) *reinterpret_cast<const uint4*>((SLOT) + 8192 * (I) + (FO))
 #define SUB8(SLOT, J, n)                                                                       \
-  {                                                                                            \
-    uint32_t flo_ = r32 * kRowBytes8 + 16 * ((2 * (J) + g) ^ (r32 & 15));                      \
-    uint32_t fhi_ = r32 * kRowBytes8 + 16 * ((8 + 2 * (J) + g) ^ (r32 & 15));                  \
-    asm volatile("" : "+v"(flo_), "+v"(fhi_));                                                 \
-    uint4 lo_[kMT], hi_[kMT];                                                                  \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                          \
-      lo_[i] = RD8(SLOT, i, flo_);                                                             \
-      hi_[i] = RD8(SLOT, i, fhi_);                                                             \
-    }                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                          \
-      acc[i][0] = mfma_fp8_fp4<J>(lo_[i], hi_[i], n##_0##J, sa_[i], n##_s0, acc[i][0]);       \
-      acc[i][1] = mfma_fp8_fp4<J>(lo_[i], hi_[i], n##_1##J, sa_[i], n##_s1, acc[i][1]);       \
-    }                                                                                          \
+  uint32_t flo_ = r32 * kRowBytes8 + 16 * ((2 * (J) + g) ^ (r32 & 15));                        \
+  uint32_t fhi_ = r32 * kRowBytes8 + 16 * ((8 + 2 * (J) + g) ^ (r32 & 15));                    \
+  asm volatile("" : "+v"(flo_), "+v"(fhi_));                                                   \
+  uint4 lo_[kMT], hi_[kMT];                                                                    \
+  _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                            \
+    lo_[i] = RD8(SLOT, i, flo_);                                                               \
+    hi_[i] = RD8(SLOT, i, fhi_);                                                               \
+  }                                                                                            \
+  _Pragma("unroll") for (int i = 0; i < kMT; ++i) {                                            \
+    acc[i][0] = mfma_fp8_fp4<J>(lo_[i], hi_[i], n##_0##J, sa_[i], n##_s0, acc[i][0]);         \
+    acc[i][1] = mfma_fp8_fp4<J>(lo_[i], hi_[i], n##_1##J, sa_[i], n##_s1, acc[i][1]);         \
   }
-#define MMA8_STAGE(SLOT, SG, SQI, n)                                                           \
+  // Half H of a stage's code loads (four of the eight).
+#define DMA_A8H(SLOT, ST, H)                                                                   \
   {                                                                                            \
-    uint32_t so_ = r32 * 16 + 4 * g;                                                           \
-    asm volatile("" : "+v"(so_));                                                              \
-    uint32_t sa_[kMT];                                                                         \
-    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 512 * ((SQI) >> 1) + 8 * ((SQI) & 1)); \
-    SUB8(SLOT, 0, n)                                                                           \
-    SUB8(SLOT, 1, n)                                                                           \
-    SUB8(SLOT, 2, n)                                                                           \
-    SUB8(SLOT, 3, n)                                                                           \
+    const uint32_t st_ = (uint32_t)opaque_stage((ST) * kRowBytes8);                            \
+    _Pragma("unroll") for (int q = 4 * (H); q < 4 * (H) + 4; ++q)                              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((q >> 2) ? xrs16 : xrs,                         \
+                                               (lds_void*)((SLOT) + 1024 * (kQPerWave8 * wave + q)), 16, \
+                                               (int)qoff[q & 3], (int)st_, 0, 0);               \
   }
+  // As in the E2M1 kernel, the loads for stage S + 1 (weights, scale group,
+  // codes, in that order) go out between stage S's MFMAs, each right after
+  // one of them, rather than in front of the first.
 #define STEP8(S, CUR, NXT, SG, SGN, BCUR, BNXT)                                                \
   {                                                                                            \
     wait_vmcnt<0>();                                                                           \
     block_barrier();                                                                           \
-    if ((S) + 1 < NST) {                                                                       \
-      DMA_LOAD_B(BNXT, (S) + 1)                                                                \
-      if (((S) + 1) % 4 == 0) { DMA_S8(SGN, ((S) + 1) / 4) }                                   \
-      DMA_A8(NXT, (S) + 1)                                                                     \
+    sched_fence();                                                                             \
+    uint32_t so_ = r32 * 16 + 4 * g;                                                           \
+    asm volatile("" : "+v"(so_));                                                              \
+    uint32_t sa_[kMT];                                                                         \
+    _Pragma("unroll") for (int i = 0; i < kMT; ++i) sa_[i] = ld4((SG) + so_ + 1024 * i + 512 * (((S) % 4) >> 1) + 8 * (((S) % 4) & 1)); \
+    {                                                                                          \
+      SUB8(CUR, 0, BCUR)                                                                       \
+      if ((S) + 1 < NST) {                                                                     \
+        DMA_W(BNXT##_00, wrs0, (S) + 1, 0) DMA_W(BNXT##_01, wrs0, (S) + 1, 1024)                \
+        DMA_W(BNXT##_02, wrs0, (S) + 1, 2048) DMA_W(BNXT##_03, wrs0, (S) + 1, 3072)             \
+        DMA_WS(BNXT##_s0, wrs0, (S) + 1)                                                       \
+        DMA_IL5(0)                                                                             \
+      }                                                                                        \
     }                                                                                          \
     sched_fence();                                                                             \
-    MMA8_STAGE(CUR, SG, (S) % 4, BCUR)                                                         \
+    {                                                                                          \
+      SUB8(CUR, 1, BCUR)                                                                       \
+      if ((S) + 1 < NST) {                                                                     \
+        DMA_W(BNXT##_10, wrs1, (S) + 1, 0) DMA_W(BNXT##_11, wrs1, (S) + 1, 1024)                \
+        DMA_W(BNXT##_12, wrs1, (S) + 1, 2048) DMA_W(BNXT##_13, wrs1, (S) + 1, 3072)             \
+        DMA_WS(BNXT##_s1, wrs1, (S) + 1)                                                       \
+        DMA_IL5(1)                                                                             \
+      }                                                                                        \
+    }                                                                                          \
+    sched_fence();                                                                             \
+    {                                                                                          \
+      SUB8(CUR, 2, BCUR)                                                                       \
+      if ((S) + 1 < NST) {                                                                     \
+        if (((S) + 1) % 4 == 0) {                                                              \
+          DMA_S8(SGN, ((S) + 1) / 4)                                                           \
+          DMA_A8H(NXT, (S) + 1, 0)                                                             \
+          DMA_IL5(2)                                                                           \
+        } else {                                                                               \
+          DMA_A8H(NXT, (S) + 1, 0)                                                             \
+          DMA_IL4(2)                                                                           \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
+    sched_fence();                                                                             \
+    {                                                                                          \
+      SUB8(CUR, 3, BCUR)                                                                       \
+      if ((S) + 1 < NST) {                                                                     \
+        DMA_A8H(NXT, (S) + 1, 1)                                                               \
+        DMA_IL4(3)                                                                             \
+      }                                                                                        \
+    }                                                                                          \
+    sched_fence();                                                                             \
   }
   // Stage s: codes in slot s % 2, weights in set s % 2, scales of group s / 4
   // in sg[(s / 4) % 2]; SGN is where the group starting at s + 1 goes.
@@ -532,7 +615,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     }
   }
 #undef STEP8
-#undef MMA8_STAGE
+#undef DMA_A8H
 #undef SUB8
 #undef RD8
 #undef DMA_S8
