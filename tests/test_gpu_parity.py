@@ -217,7 +217,8 @@ def test_act_skewed_walk_equals_row_slices(w, fp8):
     each, which takes the skewed tile walk (the first-dispatched half of the
     workgroups takes 17 consecutive tile rows, the second half 15).  Rows are
     independent, so the whole must equal the same rows transformed as 2048-row
-    slices, which take the strided walk."""
+    slices, which take the other instance (one workgroup per CU with a
+    dedicated loader wave, strided walk)."""
     note(f"case: act skewed walk vs row slices fp8={fp8}")
     wl = gen.make_workload(5, with_weights=False)
     X = dev_bf16(wl.X_bits)
@@ -228,6 +229,45 @@ def test_act_skewed_walk_equals_row_slices(w, fp8):
     for r0 in range(0, wl.M, 2048):
         qs, ss = fn(X[r0:r0 + 2048], A, B, rh, rl)
         assert torch.equal(qs, q[r0:r0 + 2048]) and torch.equal(ss, s[r0:r0 + 2048]), r0
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", ["kv4", "kv8", "weight"])
+def test_skewed_walk_cache_and_weight_modes_equal_row_slices(w, mode):
+    """The KV-cache and per-row weight instances at the skewed-walk shape
+    (16384 rows x 4096 channels) against the same rows as 2048-row slices,
+    which take the one-workgroup-per-CU instance: bit for bit.  Cache slots are
+    a permutation of the rows; the weight side gets per-row ratios."""
+    note(f"case: skewed walk vs row slices, {mode}")
+    wl = gen.make_workload(5, with_weights=False)
+    X = dev_bf16(wl.X_bits)
+    A, B = dev_f32(wl.A), dev_f32(wl.B)
+    M, K = wl.M, wl.K
+    rng = np.random.default_rng(77)
+    if mode == "weight":
+        wr_hi = dev_f32(rng.uniform(0.5, 1.0, size=(M, K // 32)))
+        wr_lo = dev_f32(rng.uniform(0.5, 1.0, size=(M, K // 32)))
+        q, s = w.weight_prep(X, A, B, wr_hi, wr_lo)
+        for r0 in range(0, M, 2048):
+            qs, ss = w.weight_prep(X[r0:r0 + 2048], A, B, wr_hi[r0:r0 + 2048], wr_lo[r0:r0 + 2048])
+            assert torch.equal(qs, q[r0:r0 + 2048]) and torch.equal(ss, s[r0:r0 + 2048]), r0
+    else:
+        fmt = 4 if mode == "kv4" else 8
+        rh, rl = dev_f32(w.clip_ratios(wl.alpha)), dev_f32(w.clip_ratios(wl.beta))
+        slots = torch.from_numpy(rng.permutation(M).astype(np.int64)).to(DEV)
+        qcols = K // 2 if fmt == 4 else K
+        caches = []
+        for sliced in (False, True):
+            cq = torch.full((M, qcols), 0xA5, dtype=torch.uint8, device=DEV)
+            cs = torch.full((M, K // 32), 0xA5, dtype=torch.uint8, device=DEV)
+            spans = range(0, M, 2048) if sliced else [0]
+            for r0 in spans:
+                r1 = r0 + 2048 if sliced else M
+                w.kv_cache_quant(X[r0:r1], A, B, rh, rl, slots[r0:r1], cq, cs, fmt=fmt)
+            caches.append((cq, cs))
+        assert torch.equal(caches[0][0], caches[1][0]) and torch.equal(caches[0][1], caches[1][1])
+        # every row was written: no sentinel scale row is left
+        assert not bool((caches[0][1] == 0xA5).all(dim=1).any())
     torch.cuda.synchronize()
 
 

@@ -39,16 +39,20 @@ namespace batq {
 namespace {
 
 constexpr int kBlocksPerWG = 8;  // one 32-channel block per compute wave; 8 blocks = 128 code bytes per row
-constexpr int kLoaderWave = kBlocksPerWG - 1;  // also issues the global -> LDS tile loads
-constexpr int kStorerWaves = 4;                // waves 0-3 also write the staged codes and scales
-constexpr int kThreads = 64 * kBlocksPerWG;
+constexpr int kStorerWaves = 4;  // waves 0-3 also write the staged codes and scales
+// The wave that issues the global -> LDS tile loads: the last compute wave, or
+// (DL) a ninth wave that does nothing else.
+template <bool DL>
+constexpr int kLoaderWave = DL ? kBlocksPerWG : kBlocksPerWG - 1;
+template <bool DL>
+constexpr int kThreads = 64 * (kBlocksPerWG + (DL ? 1 : 0));
 // Cache policy of the X loads: non-temporal (bit 1 of the buffer instructions'
 // cache-policy field), since every X byte is read once.  Measured: faster for
 // the activation and E2M1 cache paths, slower for E4M3 cache writes, which
 // keep the default policy.
 constexpr int kStreamLoad = 2;
 constexpr int kTT = 32;                        // tokens per tile (one MFMA group)
-static_assert(kLoaderWave >= kStorerWaves, "the loader issues no stores");
+static_assert(kLoaderWave<false> >= kStorerWaves, "the loader issues no stores");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -154,7 +158,7 @@ __device__ __forceinline__ PFactors load_factor_runs(const float* __restrict__ A
   return f;
 }
 
-template <bool PER_ROW, bool F8, bool STREAM>
+template <bool PER_ROW, bool F8, bool STREAM, bool DL>
 __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& p, int64_t gy, int t1) {
   using T = TQSmem<F8>;
   constexpr int kXPolicy = (F8 && STREAM) ? 0 : kStreamLoad;
@@ -193,11 +197,11 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
 
   // ---------------------------------------------------------- compute waves
   const int64_t blk = blk0 + wave;
-  const bool blk_ok = blk < nb;  // waves past the last block only keep the barriers
+  const bool blk_ok = blk < nb && wave < kBlocksPerWG;  // other waves only keep the barriers
   const int j = lane & 31;  // output channel (A-operand row) / token slot (B column)
   const int h = lane >> 5;  // which 8-channel half of each 16-channel k step
 
-  const bool loader = wave == kLoaderWave;
+  const bool loader = wave == kLoaderWave<DL>;
   // Loader: tile i (< ntile) -> its slot, kTT / 2 load instructions per tile.
   // Addressing: per-lane byte offsets within a 16-row half tile, against a
   // buffer descriptor based at that half's first row whose size ends at the
@@ -243,9 +247,11 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
       if (i < ntile) load_tile(i, i);
   }
 
-  // P_i^T as MFMA A operand, exact three-way bf16 split.
-  const PSplit ps =
-      split_p(load_factor_runs(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h));
+  // P_i^T as MFMA A operand, exact three-way bf16 split (not needed by a
+  // loader that computes no block).
+  PSplit ps{};
+  if (!(DL && loader))
+    ps = split_p(load_factor_runs(p.A, p.B + (blk_ok ? blk : 0) * (32 >> p.a_log2) * (32 >> p.a_log2), p.a_log2, j, h));
   // Ratios shared by every token (activations) are read once here.
   const bool clip = p.r_hi != nullptr;
   const bool per_row = PER_ROW && clip;
@@ -355,17 +361,77 @@ __device__ __forceinline__ void transform_quant_tiles(const TransformQuantArgs& 
   }
 }
 
+// Two instances per mode: DL = false, the loader is also a compute wave and
+// two workgroups share a CU (the skewed walk); DL = true, a ninth wave only
+// loads, one workgroup per CU (every other grid).
 template <bool PER_ROW, bool F8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
+__global__ __launch_bounds__(kThreads<false>) __attribute__((amdgpu_waves_per_eu(4))) void transform_quant_kernel(
     TransformQuantArgs p, int64_t gy, int t1) {
-  transform_quant_tiles<PER_ROW, F8, false>(p, gy, t1);
+  transform_quant_tiles<PER_ROW, F8, false, false>(p, gy, t1);
+}
+template <bool PER_ROW, bool F8>
+__global__ __launch_bounds__(kThreads<true>) __attribute__((amdgpu_waves_per_eu(5))) void transform_quant_dl_kernel(
+    TransformQuantArgs p, int64_t gy, int t1) {
+  transform_quant_tiles<PER_ROW, F8, false, true>(p, gy, t1);
 }
 
 // Cache rows are not read by the next kernel, so they are streamed past L2.
 template <bool F8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kv_cache_quant_kernel(
+__global__ __launch_bounds__(kThreads<false>) __attribute__((amdgpu_waves_per_eu(4))) void kv_cache_quant_kernel(
     TransformQuantArgs p, int64_t gy, int t1) {
-  transform_quant_tiles<false, F8, true>(p, gy, t1);
+  transform_quant_tiles<false, F8, true, false>(p, gy, t1);
+}
+template <bool F8>
+__global__ __launch_bounds__(kThreads<true>) __attribute__((amdgpu_waves_per_eu(5))) void kv_cache_quant_dl_kernel(
+    TransformQuantArgs p, int64_t gy, int t1) {
+  transform_quant_tiles<false, F8, true, true>(p, gy, t1);
+}
+
+// Grid height for a target of about `target` workgroups.  With fewer than 4
+// tiles each a workgroup's ring never fills (2048 x 4096: 10.1 us with 256
+// workgroups of 4 tiles, 11.1 us with 512 of 2), so fewer, longer workgroups
+// are used as long as there remains one per CU (smaller grids measured
+// slower).  gy is kept a multiple of 8 where it can be (see the workgroup
+// order in the kernel).
+int64_t grid_rows(int64_t gx, int64_t tiles, int64_t target) {
+  int64_t gy = target / gx;
+  if (gy >= 8) gy -= gy % 8;
+  if (gy < 1) gy = 1;
+  int64_t cap = tiles / 4;
+  if (cap >= 8) cap -= cap % 8;
+  const int64_t one_per_cu = (256 + gx - 1) / gx;
+  if (cap < one_per_cu) cap = one_per_cu;
+  if (gy > cap) gy = cap;
+  if (gy > tiles) gy = tiles;
+  return gy;
+}
+
+template <bool DL>
+void launch_instance(const TransformQuantArgs& args, dim3 grid, int64_t gy, int t1, hipStream_t stream) {
+  const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
+  const dim3 block(kThreads<DL>);
+  if (args.slot != nullptr && !per_row) {
+    if (args.fp8)
+      hipLaunchKernelGGL((DL ? kv_cache_quant_dl_kernel<true> : kv_cache_quant_kernel<true>), grid, block, 0, stream,
+                         args, gy, t1);
+    else
+      hipLaunchKernelGGL((DL ? kv_cache_quant_dl_kernel<false> : kv_cache_quant_kernel<false>), grid, block, 0, stream,
+                         args, gy, t1);
+  } else if (args.fp8) {
+    if (per_row)
+      hipLaunchKernelGGL((DL ? transform_quant_dl_kernel<true, true> : transform_quant_kernel<true, true>), grid, block,
+                         0, stream, args, gy, t1);
+    else
+      hipLaunchKernelGGL((DL ? transform_quant_dl_kernel<false, true> : transform_quant_kernel<false, true>), grid,
+                         block, 0, stream, args, gy, t1);
+  } else {
+    if (per_row)
+      hipLaunchKernelGGL((DL ? transform_quant_dl_kernel<true, false> : transform_quant_kernel<true, false>), grid,
+                         block, 0, stream, args, gy, t1);
+    else
+      hipLaunchKernelGGL((DL ? transform_quant_dl_kernel<false, false> : transform_quant_kernel<false, false>), grid,
+                         block, 0, stream, args, gy, t1);
+  }
 }
 
 }  // namespace
@@ -374,45 +440,24 @@ hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t st
   const int64_t nb = args.K >> 5;
   const int64_t gx = (nb + kBlocksPerWG - 1) / kBlocksPerWG;
   const int64_t tiles = (args.rows + kTT - 1) / kTT;
-  // Two workgroups fit per CU (70 KB of LDS each); size the grid to about one
-  // resident round and let each workgroup walk its column's tiles.
-  const int64_t target = 512;
-  int64_t gy = target / gx;
-  if (gy >= 8) gy -= gy % 8;  // see the workgroup order in the kernel
-  if (gy < 1) gy = 1;
-  // With fewer than 4 tiles each a workgroup's ring never fills (2048 x 4096:
-  // 10.1 us with 256 workgroups of 4 tiles, 11.1 us with 512 of 2), so fewer,
-  // longer workgroups are used as long as there remains one per CU (smaller
-  // grids measured slower).
-  int64_t cap = tiles / 4;
-  if (cap >= 8) cap -= cap % 8;
-  const int64_t one_per_cu = (256 + gx - 1) / gx;
-  if (cap < one_per_cu) cap = one_per_cu;
-  if (gy > cap) gy = cap;
-  if (gy > tiles) gy = tiles;
-  const dim3 grid((unsigned)(gx * gy));
-  // Skewed walk (see transform_quant_tiles) where the grid is two workgroups
-  // per CU of 16 or more equal walks: 17 tiles against 15 at 16 per
+  // Two workgroups fit per CU (70 KB of LDS each).  Where a grid of two per
+  // CU gives every workgroup 16 or more tiles of equal walks, it runs with the
+  // skewed walk (see transform_quant_tiles): 17 tiles against 15 at 16 per
   // workgroup, 4.8 % less time on 16384 x 4096 (alternating A/B).
-  int t1 = 0;
-  if (gx * gy == 512 && gy % 16 == 0 && tiles % gy == 0 && tiles / gy >= 16) t1 = (int)(tiles / gy + tiles / gy / 16);
-  const bool per_row = args.r_hi != nullptr && args.r_ld != 0;
-  if (args.slot != nullptr && !per_row) {
-    if (args.fp8)
-      hipLaunchKernelGGL((kv_cache_quant_kernel<true>), grid, dim3(kThreads), 0, stream, args, gy, t1);
-    else
-      hipLaunchKernelGGL((kv_cache_quant_kernel<false>), grid, dim3(kThreads), 0, stream, args, gy, t1);
-  } else if (args.fp8) {
-    if (per_row)
-      hipLaunchKernelGGL((transform_quant_kernel<true, true>), grid, dim3(kThreads), 0, stream, args, gy, t1);
-    else
-      hipLaunchKernelGGL((transform_quant_kernel<false, true>), grid, dim3(kThreads), 0, stream, args, gy, t1);
-  } else {
-    if (per_row)
-      hipLaunchKernelGGL((transform_quant_kernel<true, false>), grid, dim3(kThreads), 0, stream, args, gy, t1);
-    else
-      hipLaunchKernelGGL((transform_quant_kernel<false, false>), grid, dim3(kThreads), 0, stream, args, gy, t1);
+  const int64_t gy2 = grid_rows(gx, tiles, 512);
+  if (gx * gy2 == 512 && gy2 % 16 == 0 && tiles % gy2 == 0 && tiles / gy2 >= 16) {
+    const int t1 = (int)(tiles / gy2 + tiles / gy2 / 16);
+    launch_instance<false>(args, dim3((unsigned)(gx * gy2)), gy2, t1, stream);
+    return hipGetLastError();
   }
+  // Every other grid: one workgroup per CU with a dedicated loader wave,
+  // so that no compute wave waits behind a queue of tile loads.  Same codes
+  // bit for bit; alternating A/B in one process against two workgroups per
+  // CU: 2048 x 4096 9.1 -> 7.7 us (E4M3 9.9 -> 8.8), 2048 x 12288
+  // 17.7 -> 16.3 us; at 16384 x 4096 equal with E2M1 and 5 % slower with
+  // E4M3, so the skewed walk above keeps that shape.
+  const int64_t gy1 = grid_rows(gx, tiles, 256);
+  launch_instance<true>(args, dim3((unsigned)(gx * gy1)), gy1, 0, stream);
   return hipGetLastError();
 }
 
