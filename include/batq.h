@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define BATQ_ABI_VERSION 4
+#define BATQ_ABI_VERSION 5
 
 typedef enum {
   BATQ_OK = 0,
@@ -176,6 +176,16 @@ batq_status batq_mxfp4_gemm_packed(const uint8_t* Xq, const uint8_t* Xs, const u
  * activation loads (more than 256 tiles, K / 256 in {4, 8, 16, 48}, activation
  * codes under 2 GiB).  For profiling and reports; -1 on a bad shape. */
 int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8);
+
+/* Host-only query: which instance batq_act_transform_quant (and the other
+ * entry points built on the same kernel: _mxfp8, batq_weight_prep,
+ * batq_kv_cache_quant) launches for `rows` rows of K channels.  0: two
+ * workgroups per CU, each compute wave also loading, with the skewed tile
+ * walk (a grid of 512 workgroups of 16 or more equal walks); 1: one workgroup
+ * per CU with a dedicated loader wave.  Both give the same codes bit for bit.
+ * For profiling and reports; -1 on a bad shape (rows < 0, K <= 0 or
+ * K % 32 != 0). */
+int32_t batq_transform_kernel(int64_t rows, int64_t K);
 
 /* ------------------------------------------------ W4A8: MXFP8 activations
  * The pages also report a W4A8 setting: MXFP8 activations against the same

@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
               "batq_clip_ratios", "batq_abi_version", "batq_status_str", "batq_weight_packed_bytes",
               "batq_weight_pack", "batq_mxfp4_gemm_packed", "batq_act_transform_quant_mxfp8",
               "batq_mxfp8_gemm_packed", "batq_decode_workspace_bytes", "batq_w4a4_decode",
-              "batq_kv_cache_quant", "batq_packed_gemm_kernel", "batq_probe_mfma_fp4", "batq_probe_hbm_read",
+              "batq_kv_cache_quant", "batq_packed_gemm_kernel", "batq_transform_kernel", "batq_probe_mfma_fp4", "batq_probe_hbm_read",
               "batq_probe_hbm_copy", "batq_probe_stream_granule", "batq_probe_hbm_stream"):
         assert n in names
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.batq_abi_version() == 4
+    assert lib.batq_abi_version() == 5
     for s in range(8):
         assert lib.batq_status_str(s) and lib.batq_status_str(s) != b"unknown status"
     assert lib.batq_status_str(99) == b"unknown status"
@@ -150,6 +150,23 @@ def test_packed_gemm_kernel_choice(lib):
     assert f(1 << 19, 4096, 4096, 1) == 0 and f((1 << 19) - 128, 4096, 4096, 1) == 1
     assert f(0, 12288, 4096, 0) == 0
     assert f(4, 4, 100, 0) == -1 and f(-1, 4, 256, 0) == -1 and f(4, 4, 0, 0) == -1
+
+
+def test_transform_kernel_choice(lib):
+    """Two workgroups per CU with the skewed walk only where a 512-workgroup
+    grid gives every workgroup 16 or more tiles of equal walks (16 column
+    groups x 32 tile rows each: 16384 x 4096); one workgroup per CU with a
+    dedicated loader wave otherwise."""
+    f = lib.batq_transform_kernel
+    assert f(16384, 4096) == 0                              # 512 tile rows / 32 = 16 each
+    assert f(263168, 4096) == 0                             # 8224 tile rows / 32 = 257 each
+    assert f(262192, 4096) == 1                             # 8194 tile rows: ragged, unequal walks
+    assert f(16383, 4096) == 0                              # still 512 tile rows (the last one ragged)
+    assert f(2048, 4096) == 1 and f(2048, 12288) == 1 and f(32, 4096) == 1
+    assert f(16384, 1024) == 1                              # 4 column groups x 128: 4 tiles each
+    assert f(8192, 4096) == 1                               # 8 tiles each
+    assert f(0, 4096) == 1
+    assert f(-1, 4096) == -1 and f(16, 0) == -1 and f(16, 100) == -1
 
 
 def test_decode_workspace_bytes(lib):

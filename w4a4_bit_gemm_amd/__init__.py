@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     mxfp4_gemm,
     mxfp4_gemm_packed,
     packed_gemm_kernel,
+    transform_kernel,
     mxfp8_gemm_packed,
     act_transform_quant_mxfp8,
     PackedWeight,

@@ -60,6 +60,8 @@ def _load():
     lib.batq_weight_packed_bytes.argtypes = [I64, I64]
     lib.batq_weight_pack.restype = ctypes.c_int
     lib.batq_weight_pack.argtypes = [P, P, I64, I64, P, P]
+    lib.batq_transform_kernel.restype = I32
+    lib.batq_transform_kernel.argtypes = [I64, I64]
     lib.batq_mxfp4_gemm_packed.restype = ctypes.c_int
     lib.batq_mxfp4_gemm_packed.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int, P]
     lib.batq_packed_gemm_kernel.restype = I32
@@ -419,6 +421,13 @@ def mxfp8_gemm_packed(Xq8, Xs, Wp: PackedWeight, out_dtype=None, out=None):
                                         _stream_ptr(torch, Xq8.device))
     _check(st)
     return out
+
+
+def transform_kernel(rows: int, K: int) -> int:
+    """Which transform instance a shape takes (host-only query): 0 two
+    workgroups per CU with the skewed tile walk, 1 one per CU with a dedicated
+    loader wave (same codes); -1 bad shape."""
+    return int(_load().batq_transform_kernel(rows, K))
 
 
 def packed_gemm_kernel(M: int, N: int, K: int, act_fp8: bool = False) -> int:

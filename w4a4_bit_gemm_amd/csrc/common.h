@@ -52,6 +52,9 @@ struct TransformQuantArgs {
   int64_t out_rows = 0;           // rows of q / s when slot is set; other slots are skipped
 };
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream);
+// True where launch_transform_quant runs two workgroups per CU with the skewed
+// tile walk; otherwise it runs one per CU with a dedicated loader wave.
+bool transform_uses_skewed_walk(int64_t rows, int64_t K);
 
 struct GemmArgs {
   const uint8_t* xq;

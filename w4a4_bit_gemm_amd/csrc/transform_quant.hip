@@ -434,18 +434,29 @@ void launch_instance(const TransformQuantArgs& args, dim3 grid, int64_t gy, int 
   }
 }
 
+
+// Two workgroups fit per CU (70 KB of LDS each).  Where a grid of two per CU
+// gives every workgroup 16 or more tiles of equal walks, it runs with the
+// skewed walk (see transform_quant_tiles): 17 tiles against 15 at 16 per
+// workgroup, 4.8 % less time on 16384 x 4096 (alternating A/B).  Returns the
+// grid height of that case, else 0.
+int64_t skewed_grid_rows(int64_t rows, int64_t K) {
+  const int64_t gx = ((K >> 5) + kBlocksPerWG - 1) / kBlocksPerWG;
+  const int64_t tiles = (rows + kTT - 1) / kTT;
+  const int64_t gy = grid_rows(gx, tiles, 512);
+  return (gx * gy == 512 && gy % 16 == 0 && tiles % gy == 0 && tiles / gy >= 16) ? gy : 0;
+}
+
 }  // namespace
+
+bool transform_uses_skewed_walk(int64_t rows, int64_t K) { return skewed_grid_rows(rows, K) != 0; }
 
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream) {
   const int64_t nb = args.K >> 5;
   const int64_t gx = (nb + kBlocksPerWG - 1) / kBlocksPerWG;
   const int64_t tiles = (args.rows + kTT - 1) / kTT;
-  // Two workgroups fit per CU (70 KB of LDS each).  Where a grid of two per
-  // CU gives every workgroup 16 or more tiles of equal walks, it runs with the
-  // skewed walk (see transform_quant_tiles): 17 tiles against 15 at 16 per
-  // workgroup, 4.8 % less time on 16384 x 4096 (alternating A/B).
-  const int64_t gy2 = grid_rows(gx, tiles, 512);
-  if (gx * gy2 == 512 && gy2 % 16 == 0 && tiles % gy2 == 0 && tiles / gy2 >= 16) {
+  const int64_t gy2 = skewed_grid_rows(args.rows, args.K);
+  if (gy2 != 0) {
     const int t1 = (int)(tiles / gy2 + tiles / gy2 / 16);
     launch_instance<false>(args, dim3((unsigned)(gx * gy2)), gy2, t1, stream);
     return hipGetLastError();
