@@ -180,9 +180,10 @@ int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8
 /* Host-only query: which instance batq_act_transform_quant (and the other
  * entry points built on the same kernel: _mxfp8, batq_weight_prep,
  * batq_kv_cache_quant) launches for `rows` rows of K channels.  0: two
- * workgroups per CU, each compute wave also loading, with the skewed tile
- * walk (a grid of 512 workgroups of 16 or more equal walks); 1: one workgroup
- * per CU with a dedicated loader wave.  Both give the same codes bit for bit.
+ * workgroups per CU, each compute wave also loading (grids of 512 or more
+ * workgroups; with the skewed tile walk where every workgroup gets 16 or more
+ * tiles of equal walks); 1: one workgroup per CU with a dedicated loader wave
+ * (smaller grids).  Both give the same codes bit for bit.
  * For profiling and reports; -1 on a bad shape (rows < 0, K <= 0 or
  * K % 32 != 0). */
 int32_t batq_transform_kernel(int64_t rows, int64_t K);

@@ -153,19 +153,17 @@ def test_packed_gemm_kernel_choice(lib):
 
 
 def test_transform_kernel_choice(lib):
-    """Two workgroups per CU with the skewed walk only where a 512-workgroup
-    grid gives every workgroup 16 or more tiles of equal walks (16 column
-    groups x 32 tile rows each: 16384 x 4096); one workgroup per CU with a
-    dedicated loader wave otherwise."""
+    """Two workgroups per CU where that grid holds 512 workgroups (16 column
+    groups x 32 tile rows at K = 4096, each walking 4 or more tiles); one
+    workgroup per CU with a dedicated loader wave for smaller grids."""
     f = lib.batq_transform_kernel
-    assert f(16384, 4096) == 0                              # 512 tile rows / 32 = 16 each
-    assert f(263168, 4096) == 0                             # 8224 tile rows / 32 = 257 each
-    assert f(262192, 4096) == 1                             # 8194 tile rows: ragged, unequal walks
-    assert f(16383, 4096) == 0                              # still 512 tile rows (the last one ragged)
-    assert f(2048, 4096) == 1 and f(2048, 12288) == 1 and f(32, 4096) == 1
-    assert f(16384, 1024) == 1                              # 4 column groups x 128: 4 tiles each
-    assert f(8192, 4096) == 1                               # 8 tiles each
-    assert f(0, 4096) == 1
+    assert f(16384, 4096) == 0                              # 512 workgroups of 16 tiles: skewed walk
+    assert f(263168, 4096) == 0 and f(262192, 4096) == 0    # 257 tiles each; ragged
+    assert f(16383, 4096) == 0 and f(8192, 4096) == 0       # 512 workgroups of 16, of 8 tiles
+    assert f(16384, 1024) == 0                              # 4 column groups x 128 tile rows
+    assert f(2048, 4096) == 1                               # capped at 4 tiles each: 256 workgroups
+    assert f(2048, 12288) == 1                              # 48 column groups x 8: 384 workgroups
+    assert f(32, 4096) == 1 and f(0, 4096) == 1 and f(4096, 1024) == 1
     assert f(-1, 4096) == -1 and f(16, 0) == -1 and f(16, 100) == -1
 
 

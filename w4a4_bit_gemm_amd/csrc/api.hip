@@ -247,7 +247,7 @@ batq_status batq_mxfp8_gemm_packed(const uint8_t* Xq8, const uint8_t* Xs, const 
 
 int32_t batq_transform_kernel(int64_t rows, int64_t K) {
   if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
-  return batq::transform_uses_skewed_walk(rows, K) ? 0 : 1;
+  return batq::transform_uses_one_per_cu(rows, K) ? 1 : 0;
 }
 
 int32_t batq_packed_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t act_fp8) {

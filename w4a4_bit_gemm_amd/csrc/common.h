@@ -52,9 +52,10 @@ struct TransformQuantArgs {
   int64_t out_rows = 0;           // rows of q / s when slot is set; other slots are skipped
 };
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream);
-// True where launch_transform_quant runs two workgroups per CU with the skewed
-// tile walk; otherwise it runs one per CU with a dedicated loader wave.
-bool transform_uses_skewed_walk(int64_t rows, int64_t K);
+// True where launch_transform_quant runs one workgroup per CU with a dedicated
+// loader wave (grids of fewer than two workgroups per CU); otherwise it runs
+// two per CU, each compute wave also loading.
+bool transform_uses_one_per_cu(int64_t rows, int64_t K);
 
 struct GemmArgs {
   const uint8_t* xq;

@@ -438,35 +438,36 @@ void launch_instance(const TransformQuantArgs& args, dim3 grid, int64_t gy, int 
 // Two workgroups fit per CU (70 KB of LDS each).  Where a grid of two per CU
 // gives every workgroup 16 or more tiles of equal walks, it runs with the
 // skewed walk (see transform_quant_tiles): 17 tiles against 15 at 16 per
-// workgroup, 4.8 % less time on 16384 x 4096 (alternating A/B).  Returns the
-// grid height of that case, else 0.
-int64_t skewed_grid_rows(int64_t rows, int64_t K) {
-  const int64_t gx = ((K >> 5) + kBlocksPerWG - 1) / kBlocksPerWG;
-  const int64_t tiles = (rows + kTT - 1) / kTT;
-  const int64_t gy = grid_rows(gx, tiles, 512);
-  return (gx * gy == 512 && gy % 16 == 0 && tiles % gy == 0 && tiles / gy >= 16) ? gy : 0;
+// workgroup, 4.8 % less time on 16384 x 4096 (alternating A/B).
+bool skewed_walk(int64_t gx, int64_t gy, int64_t tiles) {
+  return gx * gy == 512 && gy % 16 == 0 && tiles % gy == 0 && tiles / gy >= 16;
 }
 
 }  // namespace
 
-bool transform_uses_skewed_walk(int64_t rows, int64_t K) { return skewed_grid_rows(rows, K) != 0; }
+bool transform_uses_one_per_cu(int64_t rows, int64_t K) {
+  const int64_t gx = ((K >> 5) + kBlocksPerWG - 1) / kBlocksPerWG;
+  const int64_t tiles = (rows + kTT - 1) / kTT;
+  return gx * grid_rows(gx, tiles, 512) < 512;
+}
 
 hipError_t launch_transform_quant(const TransformQuantArgs& args, hipStream_t stream) {
   const int64_t nb = args.K >> 5;
   const int64_t gx = (nb + kBlocksPerWG - 1) / kBlocksPerWG;
   const int64_t tiles = (args.rows + kTT - 1) / kTT;
-  const int64_t gy2 = skewed_grid_rows(args.rows, args.K);
-  if (gy2 != 0) {
-    const int t1 = (int)(tiles / gy2 + tiles / gy2 / 16);
+  const int64_t gy2 = grid_rows(gx, tiles, 512);
+  if (gx * gy2 >= 512) {
+    const int t1 = skewed_walk(gx, gy2, tiles) ? (int)(tiles / gy2 + tiles / gy2 / 16) : 0;
     launch_instance<false>(args, dim3((unsigned)(gx * gy2)), gy2, t1, stream);
     return hipGetLastError();
   }
-  // Every other grid: one workgroup per CU with a dedicated loader wave,
-  // so that no compute wave waits behind a queue of tile loads.  Same codes
-  // bit for bit; alternating A/B in one process against two workgroups per
-  // CU: 2048 x 4096 9.1 -> 7.7 us (E4M3 9.9 -> 8.8), 2048 x 12288
-  // 17.7 -> 16.3 us; at 16384 x 4096 equal with E2M1 and 5 % slower with
-  // E4M3, so the skewed walk above keeps that shape.
+  // Grids of fewer than two workgroups per CU: one workgroup per CU with a
+  // dedicated loader wave, so that no compute wave waits behind a queue of
+  // tile loads (with one workgroup per CU nothing else covers that wait).
+  // Same codes bit for bit; alternating A/B in one process: 2048 x 4096
+  // 9.1 -> 7.8 us (E4M3 9.9 -> 8.9 us), 2048 x 12288 17.7 -> 16.3 us.  Where
+  // two workgroups per CU fill the grid it was equal or slower (16384 x 4096
+  // equal, E4M3 5 % slower; 16384 x 1024 KV-cache writes 9-15 % slower).
   const int64_t gy1 = grid_rows(gx, tiles, 256);
   launch_instance<true>(args, dim3((unsigned)(gx * gy1)), gy1, 0, stream);
   return hipGetLastError();
