@@ -10,14 +10,19 @@ shared factor 8x8 / private 4x4; ``--config 2`` is the up/gate projection
 
 Inputs are resident in HBM when timing starts.  Steps rotate through several
 copies of every buffer (more bytes than the 256 MB Infinity Cache) so a step
-cannot be served from the cache a previous step filled.
+cannot be served from the cache a previous step filled.  Before the W warm-up
+steps, untimed steps run for at least 0.3 s: from a cold start the chip runs
+this memory-heavy workload up to 20 % slower for its first tens of
+milliseconds, so without them a short run times that ramp rather than the
+steady state (the line reports how many settling steps ran).
 
 Prints ONE JSON line.  ``value`` is the step throughput in TFLOP/s of W4A4 GEMM
 work (2 M N K per step) including the activation kernel's time.  Per-kernel
-durations come from loops of that kernel alone over the same buffers, timed
-with HIP events on the launch stream at the loops' ends only (an event between
-the two kernels of a step adds its own gap to both), and the line checks that
-they add up inside the step.  ``--ceiling`` runs only the ceiling probes (the
+durations come from loops of that kernel alone over the same buffers (direct
+C-ABI calls, each loop run once untimed first), timed with HIP events on the
+launch stream at the loops' ends only (an event between the two kernels of a
+step adds its own gap to both), and the line checks that they add up inside
+the step.  ``--ceiling`` runs only the ceiling probes (the
 FP4 matrix instruction in a register loop with the shader clock it sustains,
 HBM read and copy streams).
 """
@@ -192,6 +197,26 @@ def cpu_baseline(wl, min_seconds: float, fmt: str = "e2m1", max_rows: int = 1024
     }
 
 
+SETTLE_SECONDS = 0.3
+
+
+def settle(torch, step, min_seconds: float = SETTLE_SECONDS) -> int:
+    """Untimed steps until `min_seconds` of wall time have passed, before the
+    W warm-up steps.  From a cold start the chip runs this workload's
+    memory-bound work slowly for its first tens of milliseconds: on
+    16384 x 4096 x 4096, 20-step loops started at 195 us per step and reached
+    160 us only after about 40 ms of steps.  A GPU spin of 140 ms without
+    memory traffic, or 250 ms idle, left the same ramp; 250 ms of steps
+    removed it.  Returns the number of steps run."""
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(8):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def run_decode(args, torch, w, wl, dev):
     """The fused decode step: one w4a4_decode call, one launch (the activation
     transform, clip and MXFP4 quantisation run inside the GEMM kernel, and the
@@ -249,10 +274,12 @@ def run_decode(args, torch, w, wl, dev):
         reps = -(-steps // nsets)
         steps = reps * nsets
         run = lambda: [g.replay() for _ in range(reps)]
+        settled = settle(torch, lambda i: g.replay())
         for _ in range(max(1, -(-args.warmup // nsets))):
             g.replay()
     else:
         run = lambda: [step(i) for i in range(steps)]
+        settled = settle(torch, step)
         for i in range(args.warmup):
             step(i)
     torch.cuda.synchronize()
@@ -274,6 +301,7 @@ def run_decode(args, torch, w, wl, dev):
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
+        "settle": {"steps": settled, "min_seconds": SETTLE_SECONDS},
         "ms_per_step": wall * 1e3 / steps,
         "higher_is_better": True,
         "scaling": "weak",
@@ -335,6 +363,7 @@ def run_kv(args, torch, w, wl, dev):
         st = sets[i % nsets]
         w.kv_cache_quant(st["X"], A, B, rh, rl, st["slots"], st["q"], st["s"], fmt=fmt)
 
+    settled = settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -372,6 +401,7 @@ def run_kv(args, torch, w, wl, dev):
     kv_kernel = f"{kvk}<{'true' if fmt == 8 else 'false'}>"
     out = {
         "metric": METRIC_KV, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"steps": settled, "min_seconds": SETTLE_SECONDS},
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4" if fmt == 4 else "mxfp8", "data": "synthetic",
         "config": {"workload": f"KV-cache write: {T} tokens x {HD} channels (8 heads x 128) bf16 (t3), GPK a=8 b=4, "
@@ -693,6 +723,7 @@ def main():
         act(i)
         gemm(i)
 
+    settled = settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -731,11 +762,17 @@ def main():
         gemm_args = [(s["Xq"].data_ptr(), s["Xs"].data_ptr(), s["Wq"].data_ptr(), s["Ws"].data_ptr(), M, N, K,
                       s["Y"].data_ptr(), 0, stream) for s in sets]
 
+    # Each loop first runs once untimed: the chip's clock follows its power
+    # draw over milliseconds, and a GEMM loop that starts straight after the
+    # low-power transform loop ran its first launches faster than its own
+    # steady state (126.9 against 133.7 us on 16384 x 4096 x 4096).
     def loop_seconds(fn, fargs):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bad = 0
+        for i in range(args.steps):
+            bad |= fn(*fargs[i % nsets])
         torch.cuda.synchronize()
         e0.record()
-        bad = 0
         for i in range(args.steps):
             bad |= fn(*fargs[i % nsets])
         e1.record()
@@ -796,6 +833,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settled, "min_seconds": SETTLE_SECONDS},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
