@@ -220,6 +220,7 @@ def test_act_skewed_walk_equals_row_slices(w, fp8):
     slices, which take the other instance (one workgroup per CU with a
     dedicated loader wave, strided walk)."""
     note(f"case: act skewed walk vs row slices fp8={fp8}")
+    assert w.transform_kernel(16384, 4096) == 0 and w.transform_kernel(2048, 4096) == 1
     wl = gen.make_workload(5, with_weights=False)
     X = dev_bf16(wl.X_bits)
     A, B = dev_f32(wl.A), dev_f32(wl.B)
@@ -239,6 +240,7 @@ def test_skewed_walk_cache_and_weight_modes_equal_row_slices(w, mode):
     which take the one-workgroup-per-CU instance: bit for bit.  Cache slots are
     a permutation of the rows; the weight side gets per-row ratios."""
     note(f"case: skewed walk vs row slices, {mode}")
+    assert w.transform_kernel(16384, 4096) == 0 and w.transform_kernel(2048, 4096) == 1
     wl = gen.make_workload(5, with_weights=False)
     X = dev_bf16(wl.X_bits)
     A, B = dev_f32(wl.A), dev_f32(wl.B)
