@@ -379,7 +379,7 @@ def run_kv(args, torch, w, wl, dev):
     # The kernel alone: direct C-ABI calls with the arguments the binding
     # passes (a kernel shorter than the binding's host time per call would
     # otherwise time the host).
-    lib = w.binding._load()
+    lib = w.native_library()
     stream = torch.cuda.current_stream().cuda_stream
     rp = (0 if rh is None else rh.data_ptr(), 0 if rl is None else rl.data_ptr())
     kargs = [(st["X"].data_ptr(), T, HD, HD, A.shape[0], B.shape[1], A.data_ptr(), B.data_ptr(), rp[0], rp[1],
@@ -747,7 +747,7 @@ def main():
     # loops call the C ABI directly with the arguments the binding passes,
     # built once per buffer set: a kernel shorter than the binding's host time
     # per call (its shape and dtype checks) would otherwise time the host.
-    lib = w.binding._load()
+    lib = w.native_library()
     stream = torch.cuda.current_stream().cuda_stream
     rp = (0 if rh is None else rh.data_ptr(), 0 if rl is None else rl.data_ptr())
     act_fn = lib.batq_act_transform_quant_mxfp8 if fp8 else lib.batq_act_transform_quant

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     clip_ratios,
     gpk_invert,
     library_path,
+    native_library,
     mxfp4_gemm,
     mxfp4_gemm_packed,
     packed_gemm_kernel,

@@ -31,6 +31,13 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def native_library():
+    """The loaded ``libbatq.so`` (ctypes, argument types declared), for callers
+    that issue C-ABI calls with prepared arguments (the benchmark's per-kernel
+    loops); loads it on first use and raises if it is not built."""
+    return _load()
+
+
 def _load():
     global _lib
     if _lib is not None:
