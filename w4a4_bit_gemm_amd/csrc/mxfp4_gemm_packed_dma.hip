@@ -21,7 +21,9 @@
 //                     before its eight MFMAs (the other workgroup hides them).
 // Each wave waits only for its own loads (exact vmcnt), then one workgroup
 // barrier per stage publishes every wave's loads and frees the slot that the
-// next loads overwrite.  The output tile leaves through LDS (the ring).
+// next loads overwrite.  A bf16 output tile leaves through each wave's own
+// 4 KB of LDS, converted before staging and without a workgroup barrier; an
+// fp32 one through the ring (its own kernel instance).
 // A second kernel does the same for E4M3 activations (the W4A8 setting), with
 // 256-byte rows and a two-slot ring (see w4a8_gemm_packed_dma_kernel).
 //
@@ -45,7 +47,6 @@ constexpr int kEpiStride = 32 * kNT + 8;        // floats per staged output row
 constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes of one wave's staged 32-row band
 constexpr int kQPerWave = kSlotBytes / 1024 / 4;  // code DMA instructions per wave and stage (4)
 constexpr int kGroupM = 8;                      // row tiles per band of the tile order
-static_assert(2 * kEpiWave <= kSlotBytes + 4096, "two waves' epilogue bands fit one of the first two slots");
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ i32x8 op(uint4 v) {
@@ -150,11 +151,11 @@ __device__ __forceinline__ void tile_coords(int t, int tm, int tn, int& m, int& 
   n = (t % gsz) / gm;
 }
 
-// Output tile from the accumulators, through LDS (slot0 and slot1, both at
-// least 2 x kEpiWave bytes; the caller is done with them once every wave
-// reaches the barrier below).
-__device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT][kNT], int64_t m0, int64_t c0,
-                                           int wave, int lane, uint8_t* slot0, uint8_t* slot1) {
+// Output tile from the accumulators, through LDS: each wave stages its
+// 32-row bands at `stage` (kEpiWave bytes, in memory the ring also uses: the
+// caller is done with it once every wave reaches the barrier below).
+__device__ __forceinline__ void store_tile_at(const GemmArgs& p, f32x16 (&acc)[kMT][kNT], int64_t m0, int64_t c0,
+                                              int wave, int lane, uint8_t* stage) {
   // The accumulators are final here: an empty asm that reads them keeps the
   // last stages' MFMAs from sinking into the epilogue, which would keep their
   // operands live across it.
@@ -173,7 +174,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT]
   int64_t m0e = m0, c0e = c0;
   asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
   const int r32e = lane_e & 31, ge = lane_e >> 5;
-  float* epi = reinterpret_cast<float*>((wave_e < 2 ? slot0 : slot1) + (wave_e & 1) * kEpiWave);
+  float* epi = reinterpret_cast<float*>(stage);
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     sched_fence();
@@ -229,17 +230,90 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT]
   }
 }
 
-template <int NST>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT][kNT], int64_t m0, int64_t c0,
+                                           int wave, int lane, uint8_t* slot0, uint8_t* slot1) {
+  store_tile_at(p, acc, m0, c0, wave, lane, (wave < 2 ? slot0 : slot1) + (wave & 1) * kEpiWave);
+}
+
+// Bytes of one wave's bf16 staging band: 32 rows of the wave's 64 columns.
+constexpr int kStageRow = 2 * 32 * kNT;          // 128 bytes
+constexpr int kStageWave = 32 * kStageRow;       // 4 KB
+
+// Bf16 output tile, per wave and without a workgroup barrier: each wave
+// converts its accumulators to bf16 and stages them in its own 4 KB of LDS,
+// one 32-row band at a time, then stores 16-byte row chunks.  Lane (r, g) of
+// a 32 x 32 accumulator holds one column, so lanes r and r ^ 1 swap one
+// value per pair of rows (DPP) and each writes a bf16 pair of two adjacent
+// columns of one row: half the staged bytes and half the LDS writes of the
+// fp32 staging, and no wave waits for the others.  Dword d of staged row r
+// sits at d ^ 16 (r & 1), so that the two rows a write instruction touches
+// use disjoint banks, and a row's eight 16-byte chunks (one read
+// instruction's eight lanes) all 32.  Same conversion (round to nearest
+// even) and the same stores as store_tile_at, so the bits are the same.
+__device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, f32x16 (&acc)[kMT][kNT], int64_t m0, int64_t c0,
+                                                int wave, int lane, uint8_t* stage) {
+#pragma unroll
+  for (int i = 0; i < kMT; ++i)
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) asm volatile("" : "+a"(acc[i][k]));
+  int lane_e = lane, wave_e = wave;
+  int64_t m0e = m0, c0e = c0;
+  asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
+  const int r32 = lane_e & 31, ge = lane_e >> 5;
+  const bool odd = (r32 & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    sched_fence();
+#pragma unroll
+    for (int k = 0; k < kNT; ++k)
+#pragma unroll
+      for (int a = 0; a < 16; a += 2) {
+        // registers a, a + 1: rows 8 (a / 4) + 4 g + a % 4 and the next one
+        const float v0 = acc[i][k][a], v1 = acc[i][k][a + 1];
+        const float send = odd ? v0 : v1;
+        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+        const uint32_t w = odd ? f32x2_to_bf16x2_rne(recv, v1) : f32x2_to_bf16x2_rne(v0, recv);
+        const int row = 8 * (a >> 2) + 4 * ge + (a & 3) + (odd ? 1 : 0);
+        const int dw = (16 * k + (r32 >> 1)) ^ ((row & 1) << 4);
+        *reinterpret_cast<uint32_t*>(stage + row * kStageRow + 4 * dw) = w;
+      }
+#pragma unroll
+    for (int it = 0; it < 32 * kStageRow / 1024; ++it) {
+      const int rr = 8 * it + (lane_e >> 3);
+      const int c = lane_e & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * kStageRow + 16 * (c ^ ((rr & 1) << 2)));
+      const int64_t row = m0e + 32 * i + rr;
+      const int64_t col = c0e + 64 * wave_e + 8 * c;
+      if (row >= p.M || col >= p.N) continue;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
+      // Output stores are non-temporal, as in store_tile_at.
+      if (col + 8 <= p.N && p.vec_store) {
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+      } else {
+        const uint32_t hb[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < 8; ++e)
+          if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+// F32OUT: fp32 output through the ring slots (one epilogue per instance: with
+// both in one kernel the accumulators stayed live into each and spilled).
+template <int NST, bool F32OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mxfp4_gemm_packed_dma_kernel(
     GemmArgs p, int tiles_m, int tiles_n) {
   static_assert(NST % 4 == 0, "scale groups span four stages");
   // Separate arrays, so that the compiler sees which LDS reads each DMA can
-  // alias.  The first two slots also hold the epilogue's staged bands.
-  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes + 4096];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes + 4096];
+  // alias.  stg holds each wave's bf16 output band (fp32 output stages one
+  // wave's band in each of slot0..slot2 and stg).
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sg0[kSGroupBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sg1[kSGroupBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stg[4 * kStageWave];
+  static_assert(kEpiWave <= kSlotBytes && kEpiWave <= 4 * kStageWave, "an fp32 band fits a slot and stg");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -420,7 +494,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #undef DMA_S
 #undef DMA_A
 
-  store_tile(p, acc, m0, c0, wave, lane, slot0, slot1);
+  if constexpr (F32OUT)
+    store_tile_at(p, acc, m0, c0, wave, lane, wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : stg);
+  else
+    store_tile_bf16(p, acc, m0, c0, wave, lane, stg + wave * kStageWave);
 }
 
 // E4M3 activations x packed E2M1 weights (the W4A8 setting): the same tile,
@@ -629,9 +706,12 @@ hipError_t launch_t(const GemmArgs& args, int tiles_m, int tiles_n, hipStream_t 
   if constexpr (A8)
     hipLaunchKernelGGL((w4a8_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
                        tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
+  else if (args.out_f32)
+    hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST, true>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
                        tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST, false>), dim3(tiles_m * tiles_n), dim3(256), 0, stream,
+                       args, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
