@@ -519,7 +519,7 @@ __device__ __forceinline__ f32x16 mfma_fp8_fp4(uint4 alo, uint4 ahi, uint4 b, ui
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op(b), acc, 0, 4, J, (int)sa, J, (int)sb);
 }
 
-template <int NST>
+template <int NST, bool F32OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w4a8_gemm_packed_dma_kernel(
     GemmArgs p, int tiles_m, int tiles_n) {
   static_assert(NST % 4 == 0, "scale groups span four stages");
@@ -698,15 +698,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 #undef DMA_S8
 #undef DMA_A8
 
-  store_tile(p, acc, m0, c0, wave, lane, slot0, slot1);
+  // Stage NST - 1 (NST even) reads slot1; every wave has passed the barrier
+  // after which nothing reads or fills slot0 again, so each wave stages its
+  // bf16 band there without a workgroup barrier.
+  static_assert(NST % 2 == 0 && 4 * kStageWave <= kSlotBytes8, "bf16 bands fit the free slot");
+  if constexpr (F32OUT)
+    store_tile(p, acc, m0, c0, wave, lane, slot0, slot1);
+  else
+    store_tile_bf16(p, acc, m0, c0, wave, lane, slot0 + wave * kStageWave);
 }
 
 template <int NST, bool A8>
 hipError_t launch_t(const GemmArgs& args, int tiles_m, int tiles_n, hipStream_t stream) {
-  if constexpr (A8)
-    hipLaunchKernelGGL((w4a8_gemm_packed_dma_kernel<NST>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
-                       tiles_m, tiles_n);
-  else if (args.out_f32)
+  if constexpr (A8) {
+    if (args.out_f32)
+      hipLaunchKernelGGL((w4a8_gemm_packed_dma_kernel<NST, true>), dim3(tiles_m * tiles_n), dim3(256), 0, stream,
+                         args, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((w4a8_gemm_packed_dma_kernel<NST, false>), dim3(tiles_m * tiles_n), dim3(256), 0, stream,
+                         args, tiles_m, tiles_n);
+  } else if (args.out_f32)
     hipLaunchKernelGGL((mxfp4_gemm_packed_dma_kernel<NST, true>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, args,
                        tiles_m, tiles_n);
   else
