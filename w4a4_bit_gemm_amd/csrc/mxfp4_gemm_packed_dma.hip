@@ -261,6 +261,7 @@ __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, f32x16 (&acc)
   asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
   const int r32 = lane_e & 31, ge = lane_e >> 5;
   const bool odd = (r32 & 1) != 0;
+  const bool full = m0e + kBM <= p.M && c0e + kBN <= p.N && p.vec_store;
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     sched_fence();
@@ -277,22 +278,33 @@ __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, f32x16 (&acc)
         const int dw = (16 * k + (r32 >> 1)) ^ ((row & 1) << 4);
         *reinterpret_cast<uint32_t*>(stage + row * kStageRow + 4 * dw) = w;
       }
+    // A band's four read-backs go out together, then its stores: one wait
+    // for the reads instead of one per chunk.  A tile wholly inside Y (the
+    // usual case; the test is uniform per workgroup) stores without
+    // per-chunk bounds checks.
+    constexpr int kIt = 32 * kStageRow / 1024;
+    u32x4 v[kIt];
 #pragma unroll
-    for (int it = 0; it < 32 * kStageRow / 1024; ++it) {
+    for (int it = 0; it < kIt; ++it) {
       const int rr = 8 * it + (lane_e >> 3);
-      const int c = lane_e & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * kStageRow + 16 * (c ^ ((rr & 1) << 2)));
-      const int64_t row = m0e + 32 * i + rr;
-      const int64_t col = c0e + 64 * wave_e + 8 * c;
-      if (row >= p.M || col >= p.N) continue;
+      v[it] = *reinterpret_cast<const u32x4*>(stage + rr * kStageRow + 16 * ((lane_e & 7) ^ ((rr & 1) << 2)));
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int64_t row = m0e + 32 * i + 8 * it + (lane_e >> 3);
+      const int64_t col = c0e + 64 * wave_e + 8 * (lane_e & 7);
       uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
       // Output stores are non-temporal, as in store_tile_at.
-      if (col + 8 <= p.N && p.vec_store) {
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-      } else {
-        const uint32_t hb[4] = {v.x, v.y, v.z, v.w};
-        for (int e = 0; e < 8; ++e)
-          if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
+      if (full) {
+        __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst));
+      } else if (row < p.M && col < p.N) {
+        if (col + 8 <= p.N && p.vec_store) {
+          __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst));
+        } else {
+          const uint32_t hb[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
+        }
       }
     }
   }
