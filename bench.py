@@ -815,8 +815,8 @@ def main():
         gemm_src, gemm_kernel = "mxfp4_gemm.hip", "mxfp4_gemm_dma_kernel"
     elif w.packed_gemm_kernel(M, N, K, fp8) == 1:  # the library's own choice for this shape
         gemm_src = "mxfp4_gemm_packed_dma.hip"
-        # bf16 output: the E2M1 kernel's instance with the per-wave bf16 epilogue
-        gemm_kernel = f"w4a8_gemm_packed_dma_kernel<{nst}>" if fp8 else f"mxfp4_gemm_packed_dma_kernel<{nst},false>"
+        # bf16 output: the instance with the per-wave bf16 epilogue
+        gemm_kernel = f"{'w4a8' if fp8 else 'mxfp4'}_gemm_packed_dma_kernel<{nst},false>"
     else:
         gemm_src = "mxfp4_gemm_packed.hip"
         gemm_kernel = f"mxfp4_gemm_packed_kernel<{nst if nst in (1, 2, 4, 8, 16, 48) else 0},{gs},{a8}>"
