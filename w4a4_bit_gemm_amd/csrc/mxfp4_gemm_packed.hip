@@ -25,7 +25,7 @@
 // 128 rows apart, so when K / 256 is a multiple of 4 they are fetched four
 // stages at a time (one 16-byte load per thread instead of four 4-byte loads
 // that each touch 32 cache lines) into a two-group LDS ring.
-#include "common.h"
+#include "gemm_epilogue.h"
 
 namespace batq {
 
@@ -39,7 +39,8 @@ constexpr int kRowBytes = 128;
 constexpr int kAStage = kBM * kRowBytes;        // 16 KB
 constexpr int kAScale = kBM * 8;                // 1 KB
 constexpr int kEpiStride = 32 * kNT + 8;        // floats
-constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes
+constexpr int kEpiWave = 32 * kEpiStride * 4;   // bytes (also holds a bf16 band)
+static_assert(kEpiWave >= epi_bf16_wave_bytes<kNT>(), "a wave's bf16 band fits its fp32 band");
 constexpr int kGroupM = 8;                      // row tiles per band of the tile order
 
 __device__ __forceinline__ i32x8 op(uint4 v) {
@@ -511,7 +512,19 @@ __global__ __launch_bounds__(256) void mxfp4_gemm_packed_kernel(GemmArgs p, int 
 #undef BATQ_STEP
 #undef BATQ_CL
 
-  // Epilogue through LDS: one 32-row band per pass, 16-byte row chunks out.
+  // Bf16 output: converted before staging, in the wave's own band (the
+  // epilogue of the two-per-CU kernels).  Here, with one workgroup per CU and
+  // a private fp32 band already, it measured equal (2048 x 4096 x 12288:
+  // 46.5 against 46.4 us; the whole epilogue is 3.3 us of it).
+  if (!p.out_f32) {
+    // tile and wave are uniform; the helper takes them in scalar registers
+    const int64_t m0u = (int64_t)__builtin_amdgcn_readfirstlane(tm) * kBM;
+    const int64_t c0u = (int64_t)__builtin_amdgcn_readfirstlane(tn) * kBN;
+    store_bf16_tile(p, acc, m0u, c0u + 64 * __builtin_amdgcn_readfirstlane(wave), lane, epi_buf + wave * kEpiWave,
+                    m0u + kBM <= p.M && c0u + kBN <= p.N && p.vec_store);
+    return;
+  }
+  // Fp32 output through LDS: one 32-row band per pass, 16-byte row chunks out.
   float* epi = reinterpret_cast<float*>(epi_buf + wave * kEpiWave);
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {

@@ -30,7 +30,7 @@
 // Needs a compile-time stage count K / 256 that is a multiple of 4, and
 // activations small enough for 32-bit buffer offsets (packed_dma_applies
 // checks both on the host).
-#include "common.h"
+#include "gemm_epilogue.h"
 
 namespace batq {
 
@@ -235,80 +235,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[kMT]
   store_tile_at(p, acc, m0, c0, wave, lane, (wave < 2 ? slot0 : slot1) + (wave & 1) * kEpiWave);
 }
 
-// Bytes of one wave's bf16 staging band: 32 rows of the wave's 64 columns.
-constexpr int kStageRow = 2 * 32 * kNT;          // 128 bytes
-constexpr int kStageWave = 32 * kStageRow;       // 4 KB
-
-// Bf16 output tile, per wave and without a workgroup barrier: each wave
-// converts its accumulators to bf16 and stages them in its own 4 KB of LDS,
-// one 32-row band at a time, then stores 16-byte row chunks.  Lane (r, g) of
-// a 32 x 32 accumulator holds one column, so lanes r and r ^ 1 swap one
-// value per pair of rows (DPP) and each writes a bf16 pair of two adjacent
-// columns of one row: half the staged bytes and half the LDS writes of the
-// fp32 staging, and no wave waits for the others.  Dword d of staged row r
-// sits at d ^ 16 (r & 1), so that the two rows a write instruction touches
-// use disjoint banks, and a row's eight 16-byte chunks (one read
-// instruction's eight lanes) all 32.  Same conversion (round to nearest
-// even) and the same stores as store_tile_at, so the bits are the same.
-__device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, f32x16 (&acc)[kMT][kNT], int64_t m0, int64_t c0,
-                                                int wave, int lane, uint8_t* stage) {
-#pragma unroll
-  for (int i = 0; i < kMT; ++i)
-#pragma unroll
-    for (int k = 0; k < kNT; ++k) asm volatile("" : "+a"(acc[i][k]));
-  int lane_e = lane, wave_e = wave;
-  int64_t m0e = m0, c0e = c0;
-  asm volatile("" : "+v"(lane_e), "+s"(wave_e), "+s"(m0e), "+s"(c0e));
-  const int r32 = lane_e & 31, ge = lane_e >> 5;
-  const bool odd = (r32 & 1) != 0;
-  const bool full = m0e + kBM <= p.M && c0e + kBN <= p.N && p.vec_store;
-#pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    sched_fence();
-#pragma unroll
-    for (int k = 0; k < kNT; ++k)
-#pragma unroll
-      for (int a = 0; a < 16; a += 2) {
-        // registers a, a + 1: rows 8 (a / 4) + 4 g + a % 4 and the next one
-        const float v0 = acc[i][k][a], v1 = acc[i][k][a + 1];
-        const float send = odd ? v0 : v1;
-        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-        const uint32_t w = odd ? f32x2_to_bf16x2_rne(recv, v1) : f32x2_to_bf16x2_rne(v0, recv);
-        const int row = 8 * (a >> 2) + 4 * ge + (a & 3) + (odd ? 1 : 0);
-        const int dw = (16 * k + (r32 >> 1)) ^ ((row & 1) << 4);
-        *reinterpret_cast<uint32_t*>(stage + row * kStageRow + 4 * dw) = w;
-      }
-    // A band's four read-backs go out together, then its stores: one wait
-    // for the reads instead of one per chunk.  A tile wholly inside Y (the
-    // usual case; the test is uniform per workgroup) stores without
-    // per-chunk bounds checks.
-    constexpr int kIt = 32 * kStageRow / 1024;
-    u32x4 v[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int rr = 8 * it + (lane_e >> 3);
-      v[it] = *reinterpret_cast<const u32x4*>(stage + rr * kStageRow + 16 * ((lane_e & 7) ^ ((rr & 1) << 2)));
-    }
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int64_t row = m0e + 32 * i + 8 * it + (lane_e >> 3);
-      const int64_t col = c0e + 64 * wave_e + 8 * (lane_e & 7);
-      uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + row * p.N + col;
-      // Output stores are non-temporal, as in store_tile_at.
-      if (full) {
-        __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst));
-      } else if (row < p.M && col < p.N) {
-        if (col + 8 <= p.N && p.vec_store) {
-          __builtin_nontemporal_store(v[it], reinterpret_cast<u32x4*>(dst));
-        } else {
-          const uint32_t hb[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.N) dst[e] = (uint16_t)(hb[e >> 1] >> (16 * (e & 1)));
-        }
-      }
-    }
-  }
-}
+constexpr int kStageWave = epi_bf16_wave_bytes<kNT>();  // one wave's bf16 band (4 KB)
 
 // F32OUT: fp32 output through the ring slots (one epilogue per instance: with
 // both in one kernel the accumulators stayed live into each and spilled).
@@ -509,7 +436,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   if constexpr (F32OUT)
     store_tile_at(p, acc, m0, c0, wave, lane, wave == 0 ? slot0 : wave == 1 ? slot1 : wave == 2 ? slot2 : stg);
   else
-    store_tile_bf16(p, acc, m0, c0, wave, lane, stg + wave * kStageWave);
+    store_bf16_tile(p, acc, m0, c0 + 64 * wave, lane, stg + wave * kStageWave,
+                    m0 + kBM <= p.M && c0 + kBN <= p.N && p.vec_store);
 }
 
 // E4M3 activations x packed E2M1 weights (the W4A8 setting): the same tile,
@@ -717,7 +645,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   if constexpr (F32OUT)
     store_tile(p, acc, m0, c0, wave, lane, slot0, slot1);
   else
-    store_tile_bf16(p, acc, m0, c0, wave, lane, slot0 + wave * kStageWave);
+    store_bf16_tile(p, acc, m0, c0 + 64 * wave, lane, slot0 + wave * kStageWave,
+                    m0 + kBM <= p.M && c0 + kBN <= p.N && p.vec_store);
 }
 
 template <int NST, bool A8>
